@@ -1,0 +1,299 @@
+/*
+ * moda_oracle.c -- plain fp64 CPU oracle for the Mixture-of-Depths Attention
+ * (MoDA) forward and for the depth-stream packing permutation.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the correctness reference that the
+ * HIP path is checked against.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load it.  The product library never links
+ * it and shares no source, header, table or helper with it.
+ *
+ * Sources (the pages this follows):
+ *   [Notes]  "Mixture-of-Depths Attention: 中文研读笔记", reading notes on
+ *            arXiv 2603.15619 at cc.laoqi.cc (files/MoDA-2603.15619).
+ *   [Summ]   "Mixture-of-Depths Attention", section-by-section summary at
+ *            papercache.org.
+ *
+ * What is computed (the plain definition; no tiling, no online softmax):
+ * for every batch b, token t and query head h, with G = Hq/Hk and the shared
+ * KV head hk = floor(h/G) (0-based reading of phi(h) = ceil(h/G), [Summ] 2.1
+ * Eq. (2)), and s = 1/sqrt(d):
+ *
+ *   a_j = s * <q[b,t,h,:], k_seq[b,j,hk,:]>           j in J
+ *   b_i = s * <q[b,t,h,:], k_depth[b,t,i,hk,:]>       i in 0..L-1
+ *   J   = {0..t} if causal else {0..T-1}              ([Summ] 2.1 Eq. (2) mask)
+ *   out = (sum_j e^{a_j} v_seq[b,j,hk,:] + sum_i e^{b_i} v_depth[b,t,i,hk,:])
+ *         / (sum_j e^{a_j} + sum_i e^{b_i})
+ *   lse = log(sum_j e^{a_j} + sum_i e^{b_i})
+ *
+ * This is the unified softmax of [Notes] 二.2 (the expansion with a_j, b_i
+ * and one shared denominator) and the MoDA operator of [Summ] 2.2: both
+ * candidate sets compete in one softmax.  The depth set is the L slots that
+ * earlier layers wrote for the same token position t.  Exponentials are
+ * taken relative to the row maximum m (a change of variables that leaves the
+ * quotient unchanged); lse is reported as m + log(Z).
+ *
+ * The depth tensors are read in the generation layout [B][T][L][Hk][d]
+ * (position t's L slots stored together, [Summ] 3.2 "flash-compatible"
+ * layout, with the KV heads innermost as in [Summ] 2.1), NOT in the packed
+ * layout the GPU kernel consumes.
+ *
+ * Inputs may be fp64, fp32 or bf16 (raw 16-bit patterns); every value is
+ * widened exactly to fp64 before any arithmetic.  All accumulation is fp64.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORC_F64 = 0, ORC_F32 = 1, ORC_BF16 = 2 };
+
+/* Exact widening of one stored element to fp64.  bf16 is the top half of an
+ * IEEE binary32, so shifting its 16 bits up by 16 gives the same value. */
+static double orc_load(const void* base, size_t idx, int kind) {
+  if (kind == ORC_F64) return ((const double*)base)[idx];
+  if (kind == ORC_F32) return (double)((const float*)base)[idx];
+  uint32_t bits = (uint32_t)((const uint16_t*)base)[idx] << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+typedef struct {
+  const void *q, *k_seq, *v_seq, *k_depth, *v_depth;
+  int kind;
+  int B, T, Hq, Hk, d, L, causal;
+} orc_problem;
+
+/* Flat indices of the row-major tensors. */
+static size_t ix_q(const orc_problem* p, int b, int t, int h, int c) {
+  return (((size_t)b * p->T + t) * p->Hq + h) * p->d + c;
+}
+static size_t ix_kv(const orc_problem* p, int b, int j, int hk, int c) {
+  return (((size_t)b * p->T + j) * p->Hk + hk) * p->d + c;
+}
+static size_t ix_depth(const orc_problem* p, int b, int t, int i, int hk, int c) {
+  return ((((size_t)b * p->T + t) * p->L + i) * p->Hk + hk) * p->d + c;
+}
+
+/* One query row (b, t, h).  `work` holds T + L + d doubles. */
+static void orc_row(const orc_problem* p, int b, int t, int h, double* out_row,
+                    double* lse_out, double* work) {
+  const int G = p->Hq / p->Hk;
+  const int hk = h / G;
+  const int d = p->d;
+  const double s = 1.0 / sqrt((double)d);
+  const int nseq = p->causal ? t + 1 : p->T;
+  double* logit = work;             /* [nseq] sequence logits, then [L] depth logits */
+  double* qrow = work + p->T + p->L; /* [d] */
+
+  for (int c = 0; c < d; ++c) qrow[c] = orc_load(p->q, ix_q(p, b, t, h, c), p->kind);
+
+  /* Logits of both candidate sets, a_j then b_i ([Notes] 二.2). */
+  for (int j = 0; j < nseq; ++j) {
+    double dot = 0.0;
+    for (int c = 0; c < d; ++c) dot += qrow[c] * orc_load(p->k_seq, ix_kv(p, b, j, hk, c), p->kind);
+    logit[j] = s * dot;
+  }
+  for (int i = 0; i < p->L; ++i) {
+    double dot = 0.0;
+    for (int c = 0; c < d; ++c)
+      dot += qrow[c] * orc_load(p->k_depth, ix_depth(p, b, t, i, hk, c), p->kind);
+    logit[nseq + i] = s * dot;
+  }
+  const int ncand = nseq + p->L;
+
+  double m = -INFINITY;
+  for (int n = 0; n < ncand; ++n)
+    if (logit[n] > m) m = logit[n];
+
+  /* One shared denominator over both sets. */
+  double Z = 0.0;
+  for (int n = 0; n < ncand; ++n) {
+    logit[n] = exp(logit[n] - m); /* now the unnormalised weight */
+    Z += logit[n];
+  }
+
+  for (int c = 0; c < d; ++c) {
+    double acc = 0.0;
+    for (int j = 0; j < nseq; ++j) acc += logit[j] * orc_load(p->v_seq, ix_kv(p, b, j, hk, c), p->kind);
+    for (int i = 0; i < p->L; ++i)
+      acc += logit[nseq + i] * orc_load(p->v_depth, ix_depth(p, b, t, i, hk, c), p->kind);
+    out_row[c] = acc / Z;
+  }
+  *lse_out = m + log(Z);
+}
+
+/* ---- row lists and threading ------------------------------------------- */
+
+typedef struct {
+  const orc_problem* p;
+  const int* rows; /* nrows triples (b, t, h) */
+  long long first, last;
+  double* out;  /* [nrows][d] */
+  double* lse;  /* [nrows] */
+} orc_job;
+
+static void* orc_worker(void* arg) {
+  orc_job* job = (orc_job*)arg;
+  const orc_problem* p = job->p;
+  double* work = (double*)malloc(sizeof(double) * ((size_t)p->T + p->L + p->d));
+  if (!work) return (void*)1;
+  for (long long r = job->first; r < job->last; ++r) {
+    const int* rbth = job->rows + 3 * r;
+    orc_row(p, rbth[0], rbth[1], rbth[2], job->out + r * p->d, job->lse + r, work);
+  }
+  free(work);
+  return NULL;
+}
+
+static int orc_check(const orc_problem* p) {
+  if (!p->q || !p->k_seq || !p->v_seq) return -1;
+  if (p->L > 0 && (!p->k_depth || !p->v_depth)) return -1;
+  if (p->B <= 0 || p->T <= 0 || p->Hq <= 0 || p->Hk <= 0 || p->d <= 0 || p->L < 0) return -2;
+  if (p->Hq % p->Hk != 0) return -2;
+  if (p->causal != 0 && p->causal != 1) return -2;
+  if (p->kind < ORC_F64 || p->kind > ORC_BF16) return -3;
+  return 0;
+}
+
+static int orc_run_rows(const orc_problem* p, const int* rows, long long nrows, double* out,
+                        double* lse, int nthreads) {
+  int rc = orc_check(p);
+  if (rc) return rc;
+  for (long long r = 0; r < nrows; ++r) {
+    const int* x = rows + 3 * r;
+    if (x[0] < 0 || x[0] >= p->B || x[1] < 0 || x[1] >= p->T || x[2] < 0 || x[2] >= p->Hq) return -4;
+  }
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > nrows) nthreads = nrows > 0 ? (int)nrows : 1;
+  pthread_t* tid = (pthread_t*)malloc(sizeof(pthread_t) * nthreads);
+  orc_job* jobs = (orc_job*)malloc(sizeof(orc_job) * nthreads);
+  if (!tid || !jobs) {
+    free(tid);
+    free(jobs);
+    return -5;
+  }
+  /* Interleave rows across threads by contiguous chunks of equal count; rows
+   * are independent, so the split changes nothing in the results. */
+  for (int w = 0; w < nthreads; ++w) {
+    jobs[w].p = p;
+    jobs[w].rows = rows;
+    jobs[w].first = nrows * w / nthreads;
+    jobs[w].last = nrows * (w + 1) / nthreads;
+    jobs[w].out = out;
+    jobs[w].lse = lse;
+  }
+  int failed = 0;
+  for (int w = 1; w < nthreads; ++w)
+    if (pthread_create(&tid[w], NULL, orc_worker, &jobs[w]) != 0) {
+      tid[w] = 0; /* no thread: run this share on the calling thread */
+      if (orc_worker(&jobs[w]) != NULL) failed = 1;
+    }
+  if (orc_worker(&jobs[0]) != NULL) failed = 1;
+  for (int w = 1; w < nthreads; ++w) {
+    void* res = NULL;
+    if (tid[w]) {
+      pthread_join(tid[w], &res);
+      if (res != NULL) failed = 1;
+    }
+  }
+  free(tid);
+  free(jobs);
+  return failed ? -5 : 0;
+}
+
+/* ---- exported entry points ---------------------------------------------- */
+
+/* Selected rows.  rows = nrows triples (b, t, h); out = [nrows][d] fp64,
+ * lse = [nrows] fp64 (natural log).  kind: 0 fp64, 1 fp32, 2 bf16 inputs.
+ * Returns 0, or a negative code for bad arguments / allocation failure. */
+int moda_oracle_fwd_rows(const void* q, const void* k_seq, const void* v_seq, const void* k_depth,
+                         const void* v_depth, int kind, int B, int T, int Hq, int Hk, int d, int L,
+                         int causal, const int* rows, long long nrows, double* out, double* lse,
+                         int nthreads) {
+  orc_problem p = {q, k_seq, v_seq, k_depth, v_depth, kind, B, T, Hq, Hk, d, L, causal};
+  if (nrows < 0 || (nrows > 0 && (!rows || !out || !lse))) return -1;
+  return orc_run_rows(&p, rows, nrows, out, lse, nthreads);
+}
+
+/* Every row.  out = [B][T][Hq][d] fp64, lse = [B][Hq][T] fp64. */
+int moda_oracle_fwd(const void* q, const void* k_seq, const void* v_seq, const void* k_depth,
+                    const void* v_depth, int kind, int B, int T, int Hq, int Hk, int d, int L,
+                    int causal, double* out, double* lse, int nthreads) {
+  orc_problem p = {q, k_seq, v_seq, k_depth, v_depth, kind, B, T, Hq, Hk, d, L, causal};
+  int rc = orc_check(&p);
+  if (rc) return rc;
+  if (!out || !lse) return -1;
+  long long nrows = (long long)B * T * Hq;
+  int* rows = (int*)malloc(sizeof(int) * 3 * (size_t)nrows);
+  double* lse_rows = (double*)malloc(sizeof(double) * (size_t)nrows);
+  if (!rows || !lse_rows) {
+    free(rows);
+    free(lse_rows);
+    return -5;
+  }
+  /* Row order b, t, h matches out's [B][T][Hq][d] layout. */
+  long long r = 0;
+  for (int b = 0; b < B; ++b)
+    for (int t = 0; t < T; ++t)
+      for (int h = 0; h < Hq; ++h, ++r) {
+        rows[3 * r] = b;
+        rows[3 * r + 1] = t;
+        rows[3 * r + 2] = h;
+      }
+  rc = orc_run_rows(&p, rows, nrows, out, lse_rows, nthreads);
+  if (rc == 0) {
+    r = 0;
+    for (int b = 0; b < B; ++b)
+      for (int t = 0; t < T; ++t)
+        for (int h = 0; h < Hq; ++h, ++r) lse[((size_t)b * Hq + h) * T + t] = lse_rows[r];
+  }
+  free(rows);
+  free(lse_rows);
+  return rc;
+}
+
+/* Depth-stream packing, by definition: dst[b][t][hk][l][:] = src[b][t][l][hk][:]
+ * for elements of elem_bytes bytes.  This is the reorganisation that keeps
+ * each position's L depth states together ([Summ] 3.2), with the KV head
+ * moved outside the slot index so one (token, KV head) pair's L slots form
+ * one contiguous run. */
+int moda_oracle_pack_depth(const void* src, void* dst, int B, int T, int L, int Hk, int d,
+                           int elem_bytes) {
+  if (!src || !dst) return -1;
+  if (B <= 0 || T <= 0 || L <= 0 || Hk <= 0 || d <= 0 || elem_bytes <= 0) return -2;
+  const unsigned char* s = (const unsigned char*)src;
+  unsigned char* o = (unsigned char*)dst;
+  const size_t row = (size_t)d * elem_bytes;
+  for (int b = 0; b < B; ++b)
+    for (int t = 0; t < T; ++t)
+      for (int hk = 0; hk < Hk; ++hk)
+        for (int l = 0; l < L; ++l) {
+          size_t from = ((((size_t)b * T + t) * L + l) * Hk + hk) * row;
+          size_t to = ((((size_t)b * T + t) * Hk + hk) * L + l) * row;
+          memcpy(o + to, s + from, row);
+        }
+  return 0;
+}
+
+/* Write one layer's K or V, kv[b][t][hk][:], into slot `slot` of a packed
+ * depth tensor: dst[b][t][hk][slot][:] = kv[b][t][hk][:] (the "write" step of
+ * [Summ] 2.2: a layer appends its KV to the depth stream). */
+int moda_oracle_append_depth_slot(const void* kv, void* dst, int slot, int B, int T, int L, int Hk,
+                                  int d, int elem_bytes) {
+  if (!kv || !dst) return -1;
+  if (B <= 0 || T <= 0 || L <= 0 || Hk <= 0 || d <= 0 || elem_bytes <= 0) return -2;
+  if (slot < 0 || slot >= L) return -2;
+  const unsigned char* s = (const unsigned char*)kv;
+  unsigned char* o = (unsigned char*)dst;
+  const size_t row = (size_t)d * elem_bytes;
+  for (int b = 0; b < B; ++b)
+    for (int t = 0; t < T; ++t)
+      for (int hk = 0; hk < Hk; ++hk) {
+        size_t from = (((size_t)b * T + t) * Hk + hk) * row;
+        size_t to = ((((size_t)b * T + t) * Hk + hk) * L + slot) * row;
+        memcpy(o + to, s + from, row);
+      }
+  return 0;
+}

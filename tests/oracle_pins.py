@@ -1,0 +1,205 @@
+"""Checks that pin the fp64 oracle to things other than itself.
+
+Each function raises AssertionError when the oracle disagrees with:
+  * torch's scaled_dot_product_attention (a library routine) run on the
+    explicitly concatenated [sequence | depth] key set of every row,
+  * the reduction L=0 -> causal GQA attention (Eq. (2) of the papercache
+    summary "Mixture-of-Depths Attention", section 2.1),
+  * the pages' worked example (MoDA reading notes, section 二.2: position 3
+    with 4 depth slots -> 7 candidates, depth mass 4/7 at equal logits),
+  * closed forms (T=1, uniform logits), invariants (convex combination,
+    depth-slot permutation) and the two-branch merge identity of the MiTA
+    reading notes (section 2.3: o = (Z_c o_c + Z_r o_r) / (Z_c + Z_r)).
+
+They are shared by tests/test_oracle.py and by the planted-mistake tests,
+which rebuild the oracle with a deliberate error and require some pin to fail.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def rand_problem(B, T, Hq, Hk, d, L, seed):
+    g = torch.Generator("cpu").manual_seed(seed)
+    mk = lambda *s: torch.randn(*s, generator=g, dtype=torch.float64)  # noqa: E731
+    return (mk(B, T, Hq, d), mk(B, T, Hk, d), mk(B, T, Hk, d),
+            mk(B, T, L, Hk, d), mk(B, T, L, Hk, d))
+
+
+def sdpa_reference(q, k, v, kd, vd, causal):
+    """MoDA through torch SDPA: each row attends to cat(k_seq, k_depth[t]) with a mask.
+
+    Head h reads KV head h // G (torch.repeat_interleave).  Returns
+    (out [B,T,Hq,d], lse [B,Hq,T]) in fp64; lse comes from torch.logsumexp of
+    the masked logits.
+    """
+    B, T, Hq, d = q.shape
+    Hk = k.shape[2]
+    G = Hq // Hk
+    L = kd.shape[2]
+    ke = k.repeat_interleave(G, dim=2).permute(0, 2, 1, 3)            # [B,Hq,T,d]
+    ve = v.repeat_interleave(G, dim=2).permute(0, 2, 1, 3)
+    kde = kd.repeat_interleave(G, dim=3).permute(0, 3, 1, 2, 4)       # [B,Hq,T,L,d]
+    vde = vd.repeat_interleave(G, dim=3).permute(0, 3, 1, 2, 4)
+    kall = torch.cat([ke.unsqueeze(2).expand(B, Hq, T, T, d), kde], dim=3)  # [B,Hq,T,T+L,d]
+    vall = torch.cat([ve.unsqueeze(2).expand(B, Hq, T, T, d), vde], dim=3)
+    mask = torch.ones(T, T + L, dtype=torch.bool)
+    if causal:
+        mask[:, :T] = torch.ones(T, T, dtype=torch.bool).tril()
+    qq = q.permute(0, 2, 1, 3).unsqueeze(3)                            # [B,Hq,T,1,d]
+    m5 = mask.view(1, 1, T, 1, T + L)
+    out = F.scaled_dot_product_attention(qq, kall, vall, attn_mask=m5)  # [B,Hq,T,1,d]
+    logits = torch.matmul(qq, kall.transpose(-1, -2).contiguous()) / math.sqrt(d)
+    logits = logits.masked_fill(~m5, float("-inf"))
+    lse = torch.logsumexp(logits, dim=-1).squeeze(-1)                   # [B,Hq,T]
+    return out.squeeze(3).permute(0, 2, 1, 3).numpy(), lse.numpy()
+
+
+def pin_sdpa(B, T, Hq, Hk, d, L, causal, seed, tol=1e-12):
+    q, k, v, kd, vd = rand_problem(B, T, Hq, Hk, d, L, seed)
+    out, lse = oracle.moda_fwd(q, k, v, kd, vd, causal=causal, nthreads=2)
+    ro, rl = sdpa_reference(q, k, v, kd, vd, causal)
+    assert np.abs(out - ro).max() <= tol, "out differs from SDPA on [seq|depth] by %g" % np.abs(out - ro).max()
+    assert np.abs(lse - rl).max() <= tol, "lse differs from logsumexp by %g" % np.abs(lse - rl).max()
+
+
+def pin_l0_is_gqa(B, T, Hq, Hk, d, causal, seed, tol=1e-12):
+    """L=0: the oracle is plain GQA attention, softmax(Q_h K_phi(h)^T/sqrt(d) + M) V_phi(h)."""
+    q, k, v, _, _ = rand_problem(B, T, Hq, Hk, d, 0, seed)
+    out, _ = oracle.moda_fwd(q, k, v, None, None, causal=causal, nthreads=2)
+    G = Hq // Hk
+    ref = F.scaled_dot_product_attention(
+        q.permute(0, 2, 1, 3), k.repeat_interleave(G, dim=2).permute(0, 2, 1, 3),
+        v.repeat_interleave(G, dim=2).permute(0, 2, 1, 3), is_causal=bool(causal))
+    ref = ref.permute(0, 2, 1, 3).numpy()
+    assert np.abs(out - ref).max() <= tol, "L=0 differs from causal GQA SDPA by %g" % np.abs(out - ref).max()
+
+
+def pin_worked_example():
+    """Pages' example: equal logits (q = 0), position 3 (1-indexed), 4 depth slots -> depth mass 4/7."""
+    with open(os.path.join(GOLDEN, "worked_example.json")) as f:
+        ex = json.load(f)
+    T = ex["position_1_indexed"]       # the last row, t = T-1 (0-indexed), sees T sequence keys
+    L = ex["depth_slots"]
+    d = 4
+    q = torch.zeros(1, T, 1, d, dtype=torch.float64)
+    g = torch.Generator("cpu").manual_seed(5)
+    k = torch.randn(1, T, 1, d, generator=g, dtype=torch.float64)
+    kd = torch.randn(1, T, L, 1, d, generator=g, dtype=torch.float64)
+    v = torch.zeros(1, T, 1, d, dtype=torch.float64)     # sequence values 0
+    vd = torch.ones(1, T, L, 1, d, dtype=torch.float64)  # depth values 1 -> out = depth mass
+    out, lse = oracle.moda_fwd(q, k, v, kd, vd, causal=True, nthreads=1)
+    want = ex["depth_mass_numerator"] / ex["depth_mass_denominator"]
+    got = out[0, T - 1, 0, :]
+    assert np.abs(got - want).max() <= 1e-15, "depth mass %r, pages give 4/7" % (got[0],)
+    assert abs(lse[0, 0, T - 1] - math.log(ex["candidates"])) <= 1e-15, "lse must be log(7) at zero logits"
+    # every row t (0-indexed) then has depth mass L / (t + 1 + L)
+    for t in range(T):
+        assert abs(out[0, t, 0, 0] - L / (t + 1 + L)) <= 1e-15
+
+
+def pin_t1_closed_form(seed):
+    """T=1, L=0: one candidate, so out = v_0 and lse = q.k_0/sqrt(d) exactly."""
+    q, k, v, _, _ = rand_problem(2, 1, 4, 2, 16, 0, seed)
+    out, lse = oracle.moda_fwd(q, k, v, None, None, causal=True, nthreads=1)
+    G = 2
+    for b in range(2):
+        for h in range(4):
+            assert np.array_equal(out[b, 0, h], v[b, 0, h // G].numpy()), "T=1 L=0: out must equal v_0"
+            want = float((q[b, 0, h] * k[b, 0, h // G]).sum()) / 4.0
+            assert abs(lse[b, h, 0] - want) <= 1e-14, "T=1 L=0: lse must equal the single logit"
+
+
+def pin_t1_depth(seed):
+    """T=1: softmax over the token's own key plus its L depth keys (scipy-free closed form via torch.softmax)."""
+    L, d = 5, 8
+    q, k, v, kd, vd = rand_problem(1, 1, 2, 1, d, L, seed)
+    out, lse = oracle.moda_fwd(q, k, v, kd, vd, causal=True, nthreads=1)
+    keys = torch.cat([k[0, 0], kd[0, 0, :, 0]], dim=0)        # [1+L, d]
+    vals = torch.cat([v[0, 0], vd[0, 0, :, 0]], dim=0)
+    for h in range(2):
+        w = torch.softmax(keys @ q[0, 0, h] / math.sqrt(d), dim=0)
+        assert np.abs(out[0, 0, h] - (w @ vals).numpy()).max() <= 1e-14
+        assert abs(lse[0, h, 0] - float(torch.logsumexp(keys @ q[0, 0, h] / math.sqrt(d), 0))) <= 1e-14
+
+
+def pin_head_expansion(seed):
+    """GQA with Hk KV heads equals MHA on KV heads repeated G times (head h -> h // G)."""
+    B, T, Hq, Hk, d, L = 1, 9, 6, 2, 8, 3
+    q, k, v, kd, vd = rand_problem(B, T, Hq, Hk, d, L, seed)
+    G = Hq // Hk
+    o1, l1 = oracle.moda_fwd(q, k, v, kd, vd, nthreads=2)
+    o2, l2 = oracle.moda_fwd(q, k.repeat_interleave(G, 2), v.repeat_interleave(G, 2),
+                             kd.repeat_interleave(G, 3), vd.repeat_interleave(G, 3), nthreads=2)
+    assert np.abs(o1 - o2).max() <= 1e-14 and np.abs(l1 - l2).max() <= 1e-14
+    # G = 1: every head is an independent single-head problem
+    for h in range(Hq):
+        oh, lh = oracle.moda_fwd(q[:, :, h:h + 1], k.repeat_interleave(G, 2)[:, :, h:h + 1],
+                                 v.repeat_interleave(G, 2)[:, :, h:h + 1],
+                                 kd.repeat_interleave(G, 3)[:, :, :, h:h + 1],
+                                 vd.repeat_interleave(G, 3)[:, :, :, h:h + 1], nthreads=1)
+        assert np.abs(oh[:, :, 0] - o2[:, :, h]).max() <= 1e-14
+        assert np.abs(lh[:, 0] - l2[:, h]).max() <= 1e-14
+
+
+def pin_convex_and_permutation(seed):
+    """out is a convex combination of the visible values; permuting depth slots changes nothing."""
+    B, T, Hq, Hk, d, L = 2, 11, 4, 2, 8, 5
+    q, k, v, kd, vd = rand_problem(B, T, Hq, Hk, d, L, seed)
+    out, lse = oracle.moda_fwd(q, k, v, kd, vd, nthreads=2)
+    G = Hq // Hk
+    for b in range(B):
+        for t in range(T):
+            for h in range(Hq):
+                cand = torch.cat([v[b, : t + 1, h // G], vd[b, t, :, h // G]], dim=0).numpy()
+                lo, hi = cand.min(axis=0), cand.max(axis=0)
+                o = out[b, t, h]
+                assert np.all(o >= lo - 1e-12) and np.all(o <= hi + 1e-12), "out outside the value hull"
+    perm = torch.randperm(L, generator=torch.Generator("cpu").manual_seed(seed + 1))
+    op, lp = oracle.moda_fwd(q, k, v, kd[:, :, perm], vd[:, :, perm], nthreads=2)
+    assert np.abs(op - out).max() <= 1e-13 and np.abs(lp - lse).max() <= 1e-13
+    # a permutation applied to the keys only must change the result
+    oq, _ = oracle.moda_fwd(q, k, v, kd[:, :, perm], vd, nthreads=2)
+    assert np.abs(oq - out).max() > 1e-6
+
+
+def pin_merge_identity(seed):
+    """MoDA = (Z_s o_s + Z_d o_d) / (Z_s + Z_d) with the sequence-only result from the L=0
+    oracle and the depth-only softmax from torch SDPA; lse = logaddexp(lse_s, lse_d)."""
+    B, T, Hq, Hk, d, L = 1, 10, 4, 2, 8, 3
+    q, k, v, kd, vd = rand_problem(B, T, Hq, Hk, d, L, seed)
+    out, lse = oracle.moda_fwd(q, k, v, kd, vd, nthreads=2)
+    o_s, lse_s = oracle.moda_fwd(q, k, v, None, None, nthreads=2)
+    G = Hq // Hk
+    kde = kd.repeat_interleave(G, 3).permute(0, 3, 1, 2, 4)  # [B,Hq,T,L,d]
+    vde = vd.repeat_interleave(G, 3).permute(0, 3, 1, 2, 4)
+    qq = q.permute(0, 2, 1, 3).unsqueeze(3)                   # [B,Hq,T,1,d]
+    o_d = F.scaled_dot_product_attention(qq, kde, vde).squeeze(3).permute(0, 2, 1, 3).numpy()
+    lse_d = torch.logsumexp(torch.matmul(qq, kde.transpose(-1, -2).contiguous()).squeeze(3) / math.sqrt(d),
+                            dim=-1).numpy()                   # [B,Hq,T]
+    zs = np.exp(lse_s - lse).transpose(0, 2, 1)[..., None]    # Z_s / Z as [B,T,Hq,1]
+    zd = np.exp(lse_d - lse).transpose(0, 2, 1)[..., None]
+    merged = zs * o_s + zd * o_d
+    assert np.abs(merged - out).max() <= 1e-12, "merge identity broken by %g" % np.abs(merged - out).max()
+    assert np.abs(np.logaddexp(lse_s, lse_d) - lse).max() <= 1e-12
+
+
+def pin_depth_aligned(seed):
+    """Depth keys equal to head 0's query (plus small noise) of the SAME token must take
+    most of head 0's mass at every position; reading another token's slots would not."""
+    B, T, Hq, Hk, d, L = 1, 40, 2, 1, 32, 4
+    q, k, v, kd, vd = rand_problem(B, T, Hq, Hk, d, L, seed)
+    kd = 2.0 * q[:, :, 0:1, :].unsqueeze(2).expand(B, T, L, Hk, d) + 0.1 * kd
+    vd = torch.full_like(vd, 1.0)
+    v = torch.zeros_like(v)
+    out, _ = oracle.moda_fwd(q, k, v, kd.contiguous(), vd, nthreads=2)
+    mass = out[0, :, 0, 0]                                    # head 0, depth mass per position
+    assert mass.min() > 0.9, "depth mass of the aligned head fell to %g" % mass.min()

@@ -1,0 +1,128 @@
+"""The fp64 oracle against what the pages and the mathematics fix (CPU only)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle_pins import (pin_convex_and_permutation, pin_depth_aligned, pin_head_expansion,
+                         pin_l0_is_gqa, pin_merge_identity, pin_sdpa, pin_t1_closed_form,
+                         pin_t1_depth, pin_worked_example, rand_problem)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("G,Hk", [(1, 2), (2, 2), (4, 1), (3, 2)])
+@pytest.mark.parametrize("L", [0, 1, 3])
+def test_matches_sdpa_on_concatenated_keys(causal, G, Hk, L):
+    pin_sdpa(B=2, T=13, Hq=G * Hk, Hk=Hk, d=8, L=L, causal=causal, seed=100 + 7 * G + L)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("Hq,Hk", [(4, 2), (8, 2), (4, 4)])
+def test_l0_reduces_to_gqa_attention(causal, Hq, Hk):
+    pin_l0_is_gqa(B=2, T=17, Hq=Hq, Hk=Hk, d=16, causal=causal, seed=7 + Hq)
+
+
+def test_worked_example_from_pages():
+    pin_worked_example()
+
+
+def test_t1_closed_forms():
+    pin_t1_closed_form(3)
+    pin_t1_depth(4)
+
+
+def test_head_expansion_and_g1_per_head():
+    pin_head_expansion(11)
+
+
+def test_convex_combination_and_slot_permutation():
+    pin_convex_and_permutation(12)
+
+
+def test_merge_identity_of_two_branches():
+    pin_merge_identity(13)
+
+
+def test_depth_aligned_input_uses_same_token_depth():
+    pin_depth_aligned(14)
+
+
+def _brute_row(q, k, v, kd, vd, b, t, h, causal):
+    """Explicit [sequence | depth] concatenation with math.exp and math.fsum, tiny inputs only."""
+    B, T, Hq, d = q.shape
+    G = Hq // k.shape[2]
+    hk = h // G
+    keys = [k[b, j, hk] for j in range(t + 1 if causal else T)] + [kd[b, t, i, hk] for i in range(kd.shape[2])]
+    vals = [v[b, j, hk] for j in range(t + 1 if causal else T)] + [vd[b, t, i, hk] for i in range(kd.shape[2])]
+    logits = [math.fsum(float(q[b, t, h, c]) * float(kk[c]) for c in range(d)) / math.sqrt(d) for kk in keys]
+    mx = max(logits)
+    w = [math.exp(a - mx) for a in logits]
+    Z = math.fsum(w)
+    out = [math.fsum(wi * float(vv[c]) for wi, vv in zip(w, vals)) / Z for c in range(d)]
+    return out, mx + math.log(Z)
+
+
+def test_pure_python_brute_force():
+    q, k, v, kd, vd = rand_problem(1, 6, 4, 2, 4, 2, 21)
+    for causal in (True, False):
+        out, lse = oracle.moda_fwd(q, k, v, kd, vd, causal=causal, nthreads=1)
+        for t in range(6):
+            for h in range(4):
+                o, l = _brute_row(q.numpy(), k.numpy(), v.numpy(), kd.numpy(), vd.numpy(), 0, t, h, causal)
+                assert np.abs(out[0, t, h] - np.array(o)).max() <= 1e-13
+                assert abs(lse[0, h, t] - l) <= 1e-13
+
+
+def test_rows_api_equals_full_api():
+    q, k, v, kd, vd = rand_problem(2, 9, 4, 2, 8, 3, 22)
+    out, lse = oracle.moda_fwd(q, k, v, kd, vd, nthreads=3)
+    rows = np.array([[0, 0, 0], [1, 8, 3], [0, 4, 1], [1, 0, 2]], dtype=np.int32)
+    ro, rl = oracle.moda_fwd_rows(q, k, v, kd, vd, rows, nthreads=2)
+    for n, (b, t, h) in enumerate(rows):
+        assert np.array_equal(ro[n], out[b, t, h])
+        assert rl[n] == lse[b, h, t]
+
+
+def test_thread_count_does_not_change_results():
+    q, k, v, kd, vd = rand_problem(1, 20, 4, 2, 8, 2, 23)
+    o1, l1 = oracle.moda_fwd(q, k, v, kd, vd, nthreads=1)
+    o7, l7 = oracle.moda_fwd(q, k, v, kd, vd, nthreads=7)
+    assert np.array_equal(o1, o7) and np.array_equal(l1, l7)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_narrow_inputs_are_widened_exactly(dtype):
+    q, k, v, kd, vd = (x.to(dtype) for x in rand_problem(1, 7, 2, 1, 8, 2, 24))
+    o1, l1 = oracle.moda_fwd(q, k, v, kd, vd, nthreads=1)
+    o2, l2 = oracle.moda_fwd(*(x.double() for x in (q, k, v, kd, vd)), nthreads=1)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+@pytest.mark.parametrize("dtype", [np.float32, np.float64, np.uint16])
+def test_pack_depth_matches_numpy_transpose(dtype):
+    rng = np.random.default_rng(3)
+    src = (rng.standard_normal((2, 5, 3, 4, 8)) * 100).astype(dtype)
+    dst = oracle.pack_depth(src)
+    assert dst.dtype == src.dtype or dtype == np.float64
+    assert np.array_equal(dst.view(src.dtype), np.ascontiguousarray(src.transpose(0, 1, 3, 2, 4)))
+
+
+def test_pack_depth_hand_example():
+    # B=T=1, L=2, Hk=2, d=1: src[l][hk] = 10*l + hk  ->  dst[hk][l] = 10*l + hk
+    src = np.array([0, 1, 10, 11], dtype=np.float32).reshape(1, 1, 2, 2, 1)
+    dst = oracle.pack_depth(src)
+    assert dst.reshape(-1).tolist() == [0, 10, 1, 11]
+
+
+def test_append_depth_slot_matches_slice_assignment():
+    rng = np.random.default_rng(4)
+    dst = rng.standard_normal((2, 3, 2, 5, 4)).astype(np.float32)
+    kv = rng.standard_normal((2, 3, 2, 4)).astype(np.float32)
+    got = oracle.append_depth_slot(kv, dst, 3)
+    want = dst.copy()
+    want[:, :, :, 3, :] = kv
+    assert np.array_equal(got, want)
+    with pytest.raises(RuntimeError):
+        oracle.append_depth_slot(kv, dst, 5)
