@@ -1,0 +1,187 @@
+"""Benchmark of the MoDA fused forward on one MI355X.
+
+Workload: the long-context layer, B=1, T=65536, Hq=16, Hk=4 (G=4), d=128,
+L=48 depth slots, bf16 inputs N(0,1), causal; the same shape with L=0 is the
+causal-attention denominator (same library, same kernel family, same inputs).
+
+One step is one pass of the whole path over the resident inputs:
+  1. pack the depth K and V streams [B,T,L,Hk,d] -> [B,T,Hk,L,d],
+  2. MoDA forward with L=48,
+  3. the L=0 causal forward on the same q / k_seq / v_seq.
+W untimed warm-up steps, then K timed steps between two device
+synchronisations.  Every launch is also bracketed by HIP events on the stream
+it runs on (torch's current stream), which give each kernel's average
+duration.
+
+value = forward flops of the L=48 MoDA forward / its average kernel time
+(TFLOP/s); ratio_vs_l0 = that time / the L=0 kernel time.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from depth_stream_attention_amd import _lib, api  # noqa: E402
+from depth_stream_attention_amd import accounting as acc  # noqa: E402
+from depth_stream_attention_amd import inputs as I  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+KERNEL_SRC = os.path.join(ROOT, "depth_stream_attention_amd", "csrc", "moda_fwd_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "moda_fwd_bf16_long_L48_traffic.json")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for name in ("moda_fwd_bf16.hip", "moda_device.h"):
+        with open(os.path.join(ROOT, "depth_stream_attention_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel source; otherwise None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(shape, host, budget_s):
+    """Time the fp64 oracle (test infrastructure) on a bounded sample of rows of the same
+    workload; returns the record and the sampled rows' max error against the GPU output."""
+    import oracle
+    rng = np.random.default_rng(12345)
+    threads = oracle.default_threads()
+    done_flops, done_rows, spent = 0, 0, 0.0
+    rows_all, ref_all = [], []
+    while spent < budget_s:
+        n = 64
+        rows = np.stack([np.zeros(n, np.int64), rng.integers(0, shape.T, n), rng.integers(0, shape.Hq, n)],
+                        axis=1).astype(np.int32)
+        t0 = time.perf_counter()
+        ref, ref_lse = oracle.moda_fwd_rows(host["q"], host["k_seq"], host["v_seq"], host["k_depth"],
+                                            host["v_depth"], rows, causal=True, nthreads=threads)
+        spent += time.perf_counter() - t0
+        done_rows += n
+        done_flops += int(sum(4 * shape.d * (int(t) + 1 + shape.L) for t in rows[:, 1]))
+        rows_all.append(rows)
+        ref_all.append(ref)
+    rec = {"value": done_flops / spent / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "sample": "%d uniformly drawn (t, h) rows of the L=%d workload, %.1f s of fp64 oracle time "
+                     "on %d host threads" % (done_rows, shape.L, spent, threads)}
+    return rec, np.concatenate(rows_all), np.concatenate(ref_all)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the MoDA forward has no multi-GPU path here (each (batch, KV head) "
+              "unit is independent; see the sharding notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    _lib.ensure_built()
+    torch.cuda.set_device(0)
+
+    shape = I.workload(5, 0)
+    shape0 = I.workload(5, 1)
+    dev = I.workload_inputs(5, 0, device="cuda")
+    kd = torch.empty((shape.B, shape.T, shape.Hk, shape.L, shape.d), dtype=torch.bfloat16, device="cuda")
+    vd = torch.empty_like(kd)
+    out = torch.empty_like(dev["q"])
+    lse = torch.empty((shape.B, shape.Hq, shape.T), dtype=torch.float32, device="cuda")
+    out0 = torch.empty_like(out)
+    lse0 = torch.empty_like(lse)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        api.moda_pack_depth(dev["k_depth"], kd)
+        api.moda_pack_depth(dev["v_depth"], vd)
+        if ev: ev[1].record(stream)
+        api.moda_attn_fwd(dev["q"], dev["k_seq"], dev["v_seq"], kd, vd, causal=True, out=out, lse=lse)
+        if ev: ev[2].record(stream)
+        api.moda_attn_fwd(dev["q"], dev["k_seq"], dev["v_seq"], None, None, causal=True, out=out0, lse=lse0)
+        if ev: ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pack_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    fwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    fwd0_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
+
+    F = acc.flops(shape)
+    F0 = acc.flops(shape0)
+    Fseq = acc.flops_seq(shape.B, shape.T, shape.Hq, shape.d)
+    tflops = F / (fwd_ms * 1e-3) / 1e12
+    tflops0 = F0 / (fwd0_ms * 1e-3) / 1e12
+    traffic = measured_traffic()
+    rec = {
+        "metric": "MoDA fwd TFLOP/s + time ratio vs L=0 causal attn, bf16, T=64K, 1 MI355X",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "long-context layer B=1 T=65536 Hq=16 Hk=4 G=4 d=128 L=48 causal, "
+                               "denominator L=0", "B": shape.B, "T": shape.T, "Hq": shape.Hq, "Hk": shape.Hk,
+                   "d": shape.d, "L": shape.L, "causal": True,
+                   "step": "pack depth K,V + MoDA fwd (L=48) + causal fwd (L=0)"},
+        "fwd_ms": round(fwd_ms, 4),
+        "fwd_l0_ms": round(fwd0_ms, 4),
+        "pack_kv_ms": round(pack_ms, 4),
+        "ratio_vs_l0": round(fwd_ms / fwd0_ms, 4),
+        "l0_tflops": round(tflops0, 2),
+        "seq_mfma_util": round(Fseq / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "depth_marginal_gbs": round(acc.depth_bytes(shape) / max(1e-9, (fwd_ms - fwd0_ms) * 1e-3) / 1e9, 1),
+        "pack_gbs": round(2 * acc.depth_bytes(shape) / (pack_ms * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        host = {k: v.cpu() for k, v in dev.items()}
+        cpu, rows, ref = cpu_baseline(shape, host, args.cpu_seconds)
+        b, t, h = (torch.from_numpy(rows[:, i].astype(np.int64)).cuda() for i in range(3))
+        got = out[b, t, h].float().cpu().numpy()
+        cpu["sample_max_abs_err_vs_gpu"] = float(np.abs(got - ref).max())
+        rec["cpu_baseline"] = cpu
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,14 @@
+"""MoDA (Mixture-of-Depths Attention) fused forward for AMD Instinct MI355X (gfx950).
+
+The compute path is libmoda.so (hand-written HIP kernels behind a C ABI,
+include/moda.h); this package is its thin Python binding.
+"""
+from .api import (  # noqa: F401
+    MODAError,
+    moda_append_depth_slot,
+    moda_attn_fwd,
+    moda_attn_fwd_f32,
+    moda_block_span,
+    moda_error_string,
+    moda_pack_depth,
+)

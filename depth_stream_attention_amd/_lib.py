@@ -1,0 +1,52 @@
+"""ctypes loader for libmoda.so (the HIP kernels behind the C ABI in include/moda.h)."""
+import ctypes
+import os
+import re
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoda.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "moda.h")
+
+_lib = None
+
+
+def declared_symbols():
+    """Names of the functions include/moda.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moda_[a-z0-9_]+)\s*\(", text)))
+
+
+def load():
+    """Load libmoda.so; raise if it has not been built (there is no fallback path)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libmoda.so is not built (%s); build it with depth_stream_attention_amd.build.build() "
+                           "or __graft_entry__.build()" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int
+    fwd_args = [vp] * 5 + [i32] * 7 + [vp, vp, vp]
+    for name in ("moda_attn_fwd", "moda_attn_fwd_f32"):
+        fn = getattr(lib, name)
+        fn.argtypes = fwd_args
+        fn.restype = i32
+    lib.moda_pack_depth.argtypes = [vp, vp] + [i32] * 6 + [vp]
+    lib.moda_pack_depth.restype = i32
+    lib.moda_append_depth_slot.argtypes = [vp, vp] + [i32] * 7 + [vp]
+    lib.moda_append_depth_slot.restype = i32
+    lib.moda_block_span.argtypes = [i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.moda_block_span.restype = i32
+    lib.moda_error_string.argtypes = [i32]
+    lib.moda_error_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def ensure_built():
+    """Load the library, compiling it first only if no built copy exists."""
+    if not os.path.exists(LIB_PATH):
+        from . import build
+        build.build()
+    return load()

@@ -1,0 +1,145 @@
+"""Python binding of the C ABI (include/moda.h): argument marshalling only.
+
+Every function takes torch tensors that already live on the GPU, checks that
+their dtypes and shapes match the C signature, passes raw device pointers and
+the current HIP stream to libmoda.so, and raises MODAError on a non-zero
+return code.  All computation happens in the HIP kernels; nothing here
+computes on the host.  torch supplies device memory (out / lse when not given)
+and the stream.
+"""
+import ctypes
+
+import torch
+
+from . import _lib
+
+MODA_OK = 0
+MODA_ERR_NULL = -1
+MODA_ERR_SHAPE = -2
+MODA_ERR_UNSUPPORTED = -3
+MODA_ERR_ALIGN = -4
+MODA_ERR_HIP = -5
+
+
+class MODAError(RuntimeError):
+    def __init__(self, fn, code):
+        self.code = code
+        super().__init__("%s failed: %s (code %d)" % (fn, moda_error_string(code), code))
+
+
+def moda_error_string(code: int) -> str:
+    return _lib.load().moda_error_string(int(code)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _check(t, name, dtype, ndim):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if t.dim() != ndim:
+        raise ValueError("%s must have %d dims, got shape %s" % (name, ndim, tuple(t.shape)))
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _fwd(fn_name, dtype, q, k_seq, v_seq, k_depth, v_depth, causal, out, lse, stream):
+    _check(q, "q", dtype, 4)
+    _check(k_seq, "k_seq", dtype, 4)
+    _check(v_seq, "v_seq", dtype, 4)
+    B, T, Hq, d = q.shape
+    Hk = k_seq.shape[2]
+    if tuple(k_seq.shape) != (B, T, Hk, d) or tuple(v_seq.shape) != (B, T, Hk, d):
+        raise ValueError("k_seq / v_seq must be [B,T,Hk,d] = %s" % ((B, T, Hk, d),))
+    L = 0
+    if k_depth is not None and k_depth.numel() > 0:
+        _check(k_depth, "k_depth", dtype, 5)
+        _check(v_depth, "v_depth", dtype, 5)
+        L = k_depth.shape[3]
+        if tuple(k_depth.shape) != (B, T, Hk, L, d) or tuple(v_depth.shape) != (B, T, Hk, L, d):
+            raise ValueError("packed depth K/V must be [B,T,Hk,L,d] = %s" % ((B, T, Hk, L, d),))
+    else:
+        k_depth = v_depth = None
+    if out is None:
+        out = torch.empty((B, T, Hq, d), dtype=dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    _check(out, "out", dtype, 4)
+    _check(lse, "lse", torch.float32, 3)
+    if tuple(out.shape) != (B, T, Hq, d) or tuple(lse.shape) != (B, Hq, T):
+        raise ValueError("out must be [B,T,Hq,d] and lse [B,Hq,T]")
+    rc = getattr(_lib.load(), fn_name)(_ptr(q), _ptr(k_seq), _ptr(v_seq), _ptr(k_depth), _ptr(v_depth),
+                                       B, T, Hq, Hk, d, L, int(bool(causal)), _ptr(out), _ptr(lse),
+                                       _stream(stream))
+    if rc != MODA_OK:
+        raise MODAError(fn_name, rc)
+    return out, lse
+
+
+def moda_attn_fwd(q, k_seq, v_seq, k_depth=None, v_depth=None, causal=True, out=None, lse=None, stream=None):
+    """MoDA forward, bf16.  q [B,T,Hq,d]; k_seq, v_seq [B,T,Hk,d]; k_depth, v_depth packed
+    [B,T,Hk,L,d] (None for L = 0).  Returns (out [B,T,Hq,d] bf16, lse [B,Hq,T] fp32)."""
+    return _fwd("moda_attn_fwd", torch.bfloat16, q, k_seq, v_seq, k_depth, v_depth, causal, out, lse, stream)
+
+
+def moda_attn_fwd_f32(q, k_seq, v_seq, k_depth=None, v_depth=None, causal=True, out=None, lse=None, stream=None):
+    """MoDA forward, fp32 throughout.  Same layouts as moda_attn_fwd."""
+    return _fwd("moda_attn_fwd_f32", torch.float32, q, k_seq, v_seq, k_depth, v_depth, causal, out, lse, stream)
+
+
+def _layout_check(t, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous GPU tensor" % name)
+
+
+def moda_pack_depth(src, dst=None, stream=None):
+    """Depth-stream pack: src [B,T,L,Hk,d] -> dst [B,T,Hk,L,d] (bit copy).  Returns dst."""
+    _layout_check(src, "src")
+    if src.dim() != 5:
+        raise ValueError("src must be [B,T,L,Hk,d]")
+    B, T, L, Hk, d = src.shape
+    if dst is None:
+        dst = torch.empty((B, T, Hk, L, d), dtype=src.dtype, device=src.device)
+    _layout_check(dst, "dst")
+    if tuple(dst.shape) != (B, T, Hk, L, d) or dst.dtype != src.dtype:
+        raise ValueError("dst must be [B,T,Hk,L,d] of src's dtype")
+    rc = _lib.load().moda_pack_depth(_ptr(src), _ptr(dst), B, T, L, Hk, d, src.element_size(), _stream(stream))
+    if rc != MODA_OK:
+        raise MODAError("moda_pack_depth", rc)
+    return dst
+
+
+def moda_append_depth_slot(kv_l, dst, slot, stream=None):
+    """Write kv_l [B,T,Hk,d] into slot `slot` of the packed depth tensor dst [B,T,Hk,L,d]."""
+    _layout_check(kv_l, "kv_l")
+    _layout_check(dst, "dst")
+    if dst.dim() != 5 or kv_l.dim() != 4:
+        raise ValueError("kv_l must be [B,T,Hk,d] and dst [B,T,Hk,L,d]")
+    B, T, Hk, L, d = dst.shape
+    if tuple(kv_l.shape) != (B, T, Hk, d) or kv_l.dtype != dst.dtype:
+        raise ValueError("kv_l must be [B,T,Hk,d] of dst's dtype")
+    rc = _lib.load().moda_append_depth_slot(_ptr(kv_l), _ptr(dst), int(slot), B, T, L, Hk, d,
+                                            dst.element_size(), _stream(stream))
+    if rc != MODA_OK:
+        raise MODAError("moda_append_depth_slot", rc)
+    return dst
+
+
+def moda_block_span(row0, rows, G):
+    """(t_start, t_end) of expanded query rows [row0, row0 + rows) under group size G."""
+    a, b = ctypes.c_int(), ctypes.c_int()
+    rc = _lib.load().moda_block_span(int(row0), int(rows), int(G), ctypes.byref(a), ctypes.byref(b))
+    if rc != MODA_OK:
+        raise MODAError("moda_block_span", rc)
+    return a.value, b.value

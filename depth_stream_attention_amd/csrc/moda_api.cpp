@@ -1,0 +1,114 @@
+// C ABI of libmoda.so (declared and documented in include/moda.h).
+//
+// Every entry point validates its arguments on the host first and returns an
+// error code before touching HIP; only then does it enqueue kernels on the
+// caller's stream.  Nothing is allocated and nothing is synchronised.
+#include "../../include/moda.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <climits>
+
+#include "moda_launch.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool is_pow2_in(int x, int lo, int hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }
+
+int validate_fwd(const void* q, const void* k, const void* v, const void* kd, const void* vd, int B, int T, int Hq,
+                 int Hk, int d, int L, int causal, const void* out, const float* lse) {
+  if (!q || !k || !v || !out || !lse) return MODA_ERR_NULL;
+  if (L > 0 && (!kd || !vd)) return MODA_ERR_NULL;
+  if (B <= 0 || T <= 0 || Hq <= 0 || Hk <= 0 || d <= 0 || L < 0) return MODA_ERR_SHAPE;
+  if (Hq % Hk != 0) return MODA_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return MODA_ERR_SHAPE;
+  if (d != 64 && d != 128) return MODA_ERR_UNSUPPORTED;
+  const int G = Hq / Hk;
+  if (!is_pow2_in(G, 1, 32)) return MODA_ERR_UNSUPPORTED;
+  // Launch-size limits of this build: expanded rows and workgroup counts in int32.
+  if (static_cast<int64_t>(T) * G > INT_MAX / 2) return MODA_ERR_UNSUPPORTED;
+  if (moda::fwd_bf16_grid_blocks(B, T, Hq, Hk) > INT_MAX || moda::fwd_f32_grid_blocks(B, T, Hq) > INT_MAX)
+    return MODA_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse)) return MODA_ERR_ALIGN;
+  if (L > 0 && (!aligned16(kd) || !aligned16(vd))) return MODA_ERR_ALIGN;
+  return MODA_OK;
+}
+
+int validate_layout(const void* src, const void* dst, int B, int T, int L, int Hk, int d, int elem_bytes) {
+  if (!src || !dst) return MODA_ERR_NULL;
+  if (B <= 0 || T <= 0 || L <= 0 || Hk <= 0 || d <= 0) return MODA_ERR_SHAPE;
+  if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8) return MODA_ERR_SHAPE;
+  if (static_cast<int64_t>(B) * T > INT_MAX) return MODA_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(Hk) * L * d * elem_bytes > INT_MAX) return MODA_ERR_UNSUPPORTED;
+  if (!aligned16(src) || !aligned16(dst)) return MODA_ERR_ALIGN;
+  return MODA_OK;
+}
+
+int fwd_common(bool bf16, const void* q, const void* k, const void* v, const void* kd, const void* vd, int B, int T,
+               int Hq, int Hk, int d, int L, int causal, void* out, float* lse, moda_stream_t stream) {
+  const int rc = validate_fwd(q, k, v, kd, vd, B, T, Hq, Hk, d, L, causal, out, lse);
+  if (rc != MODA_OK) return rc;
+  moda::FwdArgs a{q, k, v, L > 0 ? kd : nullptr, L > 0 ? vd : nullptr, B, T, Hq, Hk, d, L, causal, out, lse, stream};
+  const hipError_t e = bf16 ? moda::launch_fwd_bf16(a) : moda::launch_fwd_f32(a);
+  return e == hipSuccess ? MODA_OK : MODA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moda_attn_fwd(const void* q, const void* k_seq, const void* v_seq, const void* k_depth, const void* v_depth,
+                  int B, int T, int Hq, int Hk, int d, int L, int causal, void* out, float* lse,
+                  moda_stream_t stream) {
+  return fwd_common(true, q, k_seq, v_seq, k_depth, v_depth, B, T, Hq, Hk, d, L, causal, out, lse, stream);
+}
+
+int moda_attn_fwd_f32(const void* q, const void* k_seq, const void* v_seq, const void* k_depth,
+                      const void* v_depth, int B, int T, int Hq, int Hk, int d, int L, int causal, void* out,
+                      float* lse, moda_stream_t stream) {
+  return fwd_common(false, q, k_seq, v_seq, k_depth, v_depth, B, T, Hq, Hk, d, L, causal, out, lse, stream);
+}
+
+int moda_pack_depth(const void* src, void* dst, int B, int T, int L, int Hk, int d, int elem_bytes,
+                    moda_stream_t stream) {
+  const int rc = validate_layout(src, dst, B, T, L, Hk, d, elem_bytes);
+  if (rc != MODA_OK) return rc;
+  return moda::launch_pack_depth(src, dst, B, T, L, Hk, d, elem_bytes, stream) == hipSuccess ? MODA_OK
+                                                                                               : MODA_ERR_HIP;
+}
+
+int moda_append_depth_slot(const void* kv_l, void* dst, int slot, int B, int T, int L, int Hk, int d,
+                           int elem_bytes, moda_stream_t stream) {
+  const int rc = validate_layout(kv_l, dst, B, T, L, Hk, d, elem_bytes);
+  if (rc != MODA_OK) return rc;
+  if (slot < 0 || slot >= L) return MODA_ERR_SHAPE;
+  return moda::launch_append_depth_slot(kv_l, dst, slot, B, T, L, Hk, d, elem_bytes, stream) == hipSuccess
+             ? MODA_OK
+             : MODA_ERR_HIP;
+}
+
+int moda_block_span(int row0, int rows, int G, int* t_start, int* t_end) {
+  if (!t_start || !t_end) return MODA_ERR_NULL;
+  if (row0 < 0 || rows <= 0 || G <= 0) return MODA_ERR_SHAPE;
+  if (static_cast<int64_t>(row0) + rows - 1 > INT_MAX) return MODA_ERR_SHAPE;
+  *t_start = row0 / G;
+  *t_end = (row0 + rows - 1) / G + 1;
+  return MODA_OK;
+}
+
+const char* moda_error_string(int code) {
+  switch (code) {
+    case MODA_OK: return "success";
+    case MODA_ERR_NULL: return "a required pointer is NULL";
+    case MODA_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case MODA_ERR_UNSUPPORTED: return "no kernel for this head dimension, group size or problem size";
+    case MODA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case MODA_ERR_HIP: return "the HIP launch failed";
+    default: return "unknown error";
+  }
+}
+
+}  // extern "C"

@@ -2,9 +2,16 @@
 
 This module draws random tensors and nothing else: it holds none of the
 attention arithmetic, so both the HIP path and the CPU oracle can be fed from
-it.  Every tensor is i.i.d. N(0, 1) drawn in fp32 on the host with
-``torch.Generator('cpu').manual_seed(seed)`` and then rounded once (RNE) to
-the working dtype.
+it.  Every tensor is i.i.d. N(0, 1) drawn in fp32 and then rounded once (RNE) to
+the working dtype.  Two counter-based generators are used, chosen by where
+the tensor is drawn:
+  * device="cpu": numpy's Philox4x64 bit generator with key = seed, the
+    tensor split into chunks of 2**22 elements, chunk c drawn from counter
+    (0, 0, 0, c) by Generator.standard_normal(dtype=float32).  The result does
+    not depend on how many host threads fill the chunks.
+  * device="cuda...": torch.randn with a torch.Generator on that device seeded
+    with seed (torch's Philox on the GPU).  The full-size workloads are drawn
+    this way (billions of elements); the oracle is given exact host copies.
 
 The pages benchmark their kernel on synthetic fixed shapes (MoDA reading
 notes, 三.1 kernel-benchmark row), so no dataset is involved.
@@ -18,8 +25,11 @@ variant v uses seed 1000*c + 10*v + k.  In the depth sweep (3) and the
 long-context workload (5), q / k_seq / v_seq always use v = 0, so every depth
 variant, the L=0 one included, shares one set of sequence inputs.
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, replace
 
+import numpy as np
 import torch
 
 TENSORS = ("q", "k_seq", "v_seq", "k_depth", "v_depth")
@@ -75,14 +85,37 @@ def _torch_dtype(name: str):
     return {"bf16": torch.bfloat16, "f32": torch.float32}[name]
 
 
-def _randn(shape, seed: int) -> torch.Tensor:
-    g = torch.Generator("cpu")
-    g.manual_seed(int(seed))
-    return torch.randn(tuple(shape), generator=g, dtype=torch.float32)
+_CHUNK = 1 << 22
 
 
-def make_inputs(shape: Shape, seed_of: dict, depth_aligned: bool = False):
-    """Draw q, k_seq, v_seq, k_depth, v_depth on the host for `shape`.
+def _randn(shape, seed: int, device="cpu") -> torch.Tensor:
+    device = torch.device(device)
+    if device.type != "cpu":
+        g = torch.Generator(device=device)
+        g.manual_seed(int(seed))
+        return torch.randn(tuple(shape), generator=g, device=device, dtype=torch.float32)
+    n = 1
+    for x in shape:
+        n *= int(x)
+    out = np.empty(n, np.float32)
+
+    def fill(c):
+        g = np.random.Generator(np.random.Philox(key=int(seed), counter=[0, 0, 0, c]))
+        lo = c * _CHUNK
+        g.standard_normal(min(n, lo + _CHUNK) - lo, dtype=np.float32, out=out[lo:lo + _CHUNK])
+
+    nchunks = (n + _CHUNK - 1) // _CHUNK
+    if nchunks <= 1:
+        if n:
+            fill(0)
+    else:
+        with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1, nchunks)) as ex:
+            list(ex.map(fill, range(nchunks)))
+    return torch.from_numpy(out).view(tuple(int(x) for x in shape))
+
+
+def make_inputs(shape: Shape, seed_of: dict, depth_aligned: bool = False, device="cpu"):
+    """Draw q, k_seq, v_seq, k_depth, v_depth on `device` for `shape`.
 
     seed_of maps each tensor name to its seed.  With L == 0 the depth tensors
     are empty ([B,T,0,Hk,d]).  depth_aligned=True builds the stress input in
@@ -91,18 +124,18 @@ def make_inputs(shape: Shape, seed_of: dict, depth_aligned: bool = False):
     """
     s = shape
     dt = _torch_dtype(s.dtype)
-    q = _randn((s.B, s.T, s.Hq, s.d), seed_of["q"])
-    k = _randn((s.B, s.T, s.Hk, s.d), seed_of["k_seq"])
-    v = _randn((s.B, s.T, s.Hk, s.d), seed_of["v_seq"])
+    q = _randn((s.B, s.T, s.Hq, s.d), seed_of["q"], device)
+    k = _randn((s.B, s.T, s.Hk, s.d), seed_of["k_seq"], device)
+    v = _randn((s.B, s.T, s.Hk, s.d), seed_of["v_seq"], device)
     if s.L > 0:
-        kd = _randn((s.B, s.T, s.L, s.Hk, s.d), seed_of["k_depth"])
-        vd = _randn((s.B, s.T, s.L, s.Hk, s.d), seed_of["v_depth"])
+        kd = _randn((s.B, s.T, s.L, s.Hk, s.d), seed_of["k_depth"], device)
+        vd = _randn((s.B, s.T, s.L, s.Hk, s.d), seed_of["v_depth"], device)
         if depth_aligned:
             lead = q[:, :, :: s.G, :]  # [B,T,Hk,d]: head hk*G of each KV group
             kd = lead.unsqueeze(2) + 0.5 * kd
     else:
-        kd = torch.empty((s.B, s.T, 0, s.Hk, s.d), dtype=torch.float32)
-        vd = torch.empty((s.B, s.T, 0, s.Hk, s.d), dtype=torch.float32)
+        kd = torch.empty((s.B, s.T, 0, s.Hk, s.d), dtype=torch.float32, device=device)
+        vd = torch.empty((s.B, s.T, 0, s.Hk, s.d), dtype=torch.float32, device=device)
     if s.key_scale != 1.0:
         k = k * s.key_scale
         kd = kd * s.key_scale
@@ -110,13 +143,13 @@ def make_inputs(shape: Shape, seed_of: dict, depth_aligned: bool = False):
             "k_depth": kd.to(dt), "v_depth": vd.to(dt)}
 
 
-def workload_inputs(c: int, v: int = 0, depth_aligned: bool = False):
-    return make_inputs(workload(c, v), seeds(c, v), depth_aligned=depth_aligned)
+def workload_inputs(c: int, v: int = 0, depth_aligned: bool = False, device="cpu"):
+    return make_inputs(workload(c, v), seeds(c, v), depth_aligned=depth_aligned, device=device)
 
 
-def random_inputs(shape: Shape, seed: int, depth_aligned: bool = False):
+def random_inputs(shape: Shape, seed: int, depth_aligned: bool = False, device="cpu"):
     """Inputs for an ad-hoc shape: tensor k uses seed + k."""
-    return make_inputs(shape, {n: seed + k for k, n in enumerate(TENSORS)}, depth_aligned)
+    return make_inputs(shape, {n: seed + k for k, n in enumerate(TENSORS)}, depth_aligned, device)
 
 
 def with_(shape: Shape, **kw) -> Shape:

@@ -1,0 +1,139 @@
+/*
+ * moda.h -- C ABI of libmoda.so: the Mixture-of-Depths Attention (MoDA)
+ * fused forward and the depth-stream layout kernels for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * Sources of the operations (cited by page title and section):
+ *   [Notes] "Mixture-of-Depths Attention: 中文研读笔记" (reading notes on
+ *           arXiv 2603.15619, cc.laoqi.cc).
+ *   [Summ]  "Mixture-of-Depths Attention" (section-by-section summary,
+ *           papercache.org).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library allocates no memory, keeps no state between calls and never
+ *     synchronises: work is enqueued on `stream` (a hipStream_t; NULL means
+ *     the default stream) and the call returns before it runs.
+ *   - Tensors are dense, row-major, with no strides.  Indices are 0-based.
+ *   - Every pointer must be 16-byte aligned.
+ *   - Arguments are validated on the host before any HIP call, so each error
+ *     code below can be produced without a GPU.  On error nothing is
+ *     enqueued and the outputs are untouched.  No C++ exception crosses the
+ *     ABI.
+ *   - Results are deterministic: fixed reduction order, no atomics.
+ */
+#ifndef MODA_H
+#define MODA_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define MODA_OK 0
+#define MODA_ERR_NULL (-1)        /* a required pointer is NULL */
+#define MODA_ERR_SHAPE (-2)       /* a size is out of range or inconsistent */
+#define MODA_ERR_UNSUPPORTED (-3) /* a valid size this build has no kernel for */
+#define MODA_ERR_ALIGN (-4)       /* a pointer is not 16-byte aligned */
+#define MODA_ERR_HIP (-5)         /* the HIP launch reported an error */
+
+typedef void* moda_stream_t; /* hipStream_t */
+
+/*
+ * MoDA forward, bf16 in / bf16 out, fp32 accumulation.
+ *
+ * Operation ([Notes] 二.2 unified-softmax expansion; [Summ] 2.2 MoDA and
+ * 3.3 Algorithm 1): for batch b, token t and query head h, with
+ * G = Hq / Hk, KV head hk = floor(h / G) (0-based form of phi(h) = ceil(h/G),
+ * [Summ] 2.1 Eq. (2)) and s = 1/sqrt(d), one softmax runs jointly over
+ *   - the sequence keys j of KV head hk: j <= t when causal = 1 (the causal
+ *     mask of Eq. (2)), all j < T when causal = 0, with logit
+ *     s * <q[b,t,h], k_seq[b,j,hk]> and value v_seq[b,j,hk];
+ *   - the L depth slots i of the same token t and KV head hk, with logit
+ *     s * <q[b,t,h], k_depth[b,t,hk,i]> and value v_depth[b,t,hk,i].
+ *   out[b,t,h,:] = sum(e^logit * value) / sum(e^logit), over both sets;
+ *   lse[b,h,t]   = log(sum(e^logit)) (natural log, fp32).
+ *
+ * Arguments
+ *   q        [B][T][Hq][d] bf16
+ *   k_seq    [B][T][Hk][d] bf16
+ *   v_seq    [B][T][Hk][d] bf16
+ *   k_depth  [B][T][Hk][L][d] bf16, the PACKED depth layout written by
+ *            moda_pack_depth / moda_append_depth_slot.  May be NULL iff L == 0.
+ *   v_depth  [B][T][Hk][L][d] bf16, same layout and rule.
+ *   B, T, Hq, Hk, d, L   sizes; L = number of depth slots (may be 0).
+ *   causal   1 = causal sequence mask, 0 = full sequence attention.
+ *   out      [B][T][Hq][d] bf16 (written, round-to-nearest-even).
+ *   lse      [B][Hq][T] fp32 (written).
+ *   stream   HIP stream to enqueue on.
+ * out and lse must not overlap any input.
+ *
+ * Errors: MODA_ERR_NULL (q, k_seq, v_seq, out or lse NULL; depth NULL with
+ * L > 0); MODA_ERR_SHAPE (B, T, Hq, Hk or d <= 0, L < 0, Hq % Hk != 0,
+ * causal not 0/1); MODA_ERR_UNSUPPORTED (d not 64 or 128; G not in
+ * {1,2,4,8,16,32}); MODA_ERR_ALIGN; MODA_ERR_HIP.
+ */
+int moda_attn_fwd(const void* q, const void* k_seq, const void* v_seq, const void* k_depth,
+                  const void* v_depth, int B, int T, int Hq, int Hk, int d, int L, int causal,
+                  void* out, float* lse, moda_stream_t stream);
+
+/*
+ * The same operation with fp32 inputs and fp32 output, computed in fp32.
+ * Arguments, layouts and errors are those of moda_attn_fwd with every bf16
+ * tensor replaced by an fp32 one.
+ */
+int moda_attn_fwd_f32(const void* q, const void* k_seq, const void* v_seq, const void* k_depth,
+                      const void* v_depth, int B, int T, int Hq, int Hk, int d, int L, int causal,
+                      void* out, float* lse, moda_stream_t stream);
+
+/*
+ * Depth-stream pack: dst[b][t][hk][l][:] = src[b][t][l][hk][:], bit for bit.
+ *
+ * [Summ] 3.2 stores a position's L depth states contiguously; this layout
+ * additionally moves the KV head outside the slot index, so the L slots of one
+ * (token, KV head) pair form one contiguous run of L*d elements that the
+ * forward stages once for that head's G query rows ([Summ] 3.2 group-aware
+ * depth computation).
+ *
+ *   src  [B][T][L][Hk][d] elements of elem_bytes bytes (read).
+ *   dst  [B][T][Hk][L][d] (written).  Must not overlap src.
+ *   elem_bytes  1, 2, 4 or 8 (2 for bf16, 4 for fp32).
+ * Errors: MODA_ERR_NULL; MODA_ERR_SHAPE (a size <= 0 or a bad elem_bytes);
+ * MODA_ERR_ALIGN; MODA_ERR_HIP.
+ */
+int moda_pack_depth(const void* src, void* dst, int B, int T, int L, int Hk, int d, int elem_bytes,
+                    moda_stream_t stream);
+
+/*
+ * Write one layer's K (or V) into one slot of the packed depth stream:
+ * dst[b][t][hk][slot][:] = kv_l[b][t][hk][:] ([Summ] 2.2: after its
+ * attention, a layer appends its KV to the depth stream for later layers).
+ * Other slots of dst are left untouched.
+ *
+ *   kv_l  [B][T][Hk][d] (read).
+ *   dst   [B][T][Hk][L][d] (slot `slot` written).  Must not overlap kv_l.
+ *   slot  in [0, L).
+ * Errors: MODA_ERR_NULL; MODA_ERR_SHAPE (a size <= 0, slot out of range,
+ * bad elem_bytes); MODA_ERR_ALIGN; MODA_ERR_HIP.
+ */
+int moda_append_depth_slot(const void* kv_l, void* dst, int slot, int B, int T, int L, int Hk, int d,
+                           int elem_bytes, moda_stream_t stream);
+
+/*
+ * Base-time span of a block of expanded query rows ([Summ] 3.3, algorithm
+ * preparation; [Notes] 二.5).  Expanded row i_q = t*G + g holds token t,
+ * head g of one KV group, so t_base(i_q) = floor(i_q / G).  For the rows
+ * [row0, row0 + rows): *t_start = min t_base = floor(row0 / G) and
+ * *t_end = max t_base + 1 = floor((row0 + rows - 1) / G) + 1.  Host only.
+ * Errors: MODA_ERR_NULL; MODA_ERR_SHAPE (row0 < 0, rows <= 0, G <= 0).
+ */
+int moda_block_span(int row0, int rows, int G, int* t_start, int* t_end);
+
+/* Static, human-readable text for a return code ("unknown error" otherwise). */
+const char* moda_error_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MODA_H */

@@ -1,0 +1,94 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol, and every
+validation error is produced on the host before any HIP call."""
+import ctypes
+import json
+import os
+
+import pytest
+
+from depth_stream_attention_amd import _lib
+from depth_stream_attention_amd import api
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+A = ctypes.c_void_p(0x10000)      # aligned fake device addresses: never dereferenced,
+A2 = ctypes.c_void_p(0x20000)     # validation fails before any HIP call
+MIS = ctypes.c_void_p(0x10008)    # 8-byte aligned only
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.ensure_built()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _lib.declared_symbols()
+    assert {"moda_attn_fwd", "moda_attn_fwd_f32", "moda_pack_depth", "moda_append_depth_slot",
+            "moda_error_string", "moda_block_span"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), "libmoda.so does not export %s" % n
+
+
+def test_error_strings(lib):
+    for code in (0, -1, -2, -3, -4, -5):
+        s = api.moda_error_string(code)
+        assert s and s != "unknown error"
+    assert api.moda_error_string(17) == "unknown error"
+
+
+def fwd(lib, name="moda_attn_fwd", q=A, k=A, v=A, kd=A, vd=A, B=1, T=16, Hq=4, Hk=2, d=128, L=2,
+        causal=1, out=A2, lse=A2):
+    return getattr(lib, name)(q, k, v, kd, vd, B, T, Hq, Hk, d, L, causal, out, lse, None)
+
+
+@pytest.mark.parametrize("name", ["moda_attn_fwd", "moda_attn_fwd_f32"])
+def test_fwd_validation(lib, name):
+    N, S, U, AL = api.MODA_ERR_NULL, api.MODA_ERR_SHAPE, api.MODA_ERR_UNSUPPORTED, api.MODA_ERR_ALIGN
+    f = lambda **kw: fwd(lib, name, **kw)  # noqa: E731
+    assert f(q=None) == N and f(k=None) == N and f(v=None) == N
+    assert f(out=None) == N and f(lse=None) == N
+    assert f(kd=None) == N and f(vd=None) == N
+    assert f(kd=None, vd=None, L=0) != N              # depth may be NULL when L == 0
+    for kw in ({"B": 0}, {"T": 0}, {"Hq": 0}, {"Hk": 0}, {"d": 0}, {"L": -1}, {"Hq": 6, "Hk": 4},
+               {"causal": 2}, {"causal": -1}):
+        assert f(**kw) == S, kw
+    for kw in ({"d": 96}, {"d": 256}, {"Hq": 6, "Hk": 2}, {"Hq": 128, "Hk": 2}):
+        assert f(**kw) == U, kw
+    for kw in ({"q": MIS}, {"k": MIS}, {"v": MIS}, {"kd": MIS}, {"vd": MIS}, {"out": MIS}, {"lse": MIS}):
+        assert f(**kw) == AL, kw
+    assert f(kd=MIS, vd=MIS, L=0) != AL                # depth pointers are ignored when L == 0
+    assert f(T=(1 << 30), Hq=32, Hk=1) == U            # expanded rows beyond int32 launch limits
+
+
+def test_layout_validation(lib):
+    N, S, AL = api.MODA_ERR_NULL, api.MODA_ERR_SHAPE, api.MODA_ERR_ALIGN
+    p = lambda src=A, dst=A2, B=1, T=4, L=3, Hk=2, d=128, eb=2: lib.moda_pack_depth(  # noqa: E731
+        src, dst, B, T, L, Hk, d, eb, None)
+    assert p(src=None) == N and p(dst=None) == N
+    for kw in ({"B": 0}, {"T": -1}, {"L": 0}, {"Hk": 0}, {"d": 0}, {"eb": 3}, {"eb": 0}):
+        assert p(**kw) == S, kw
+    assert p(src=MIS) == AL and p(dst=MIS) == AL
+    a = lambda kv=A, dst=A2, slot=0, B=1, T=4, L=3, Hk=2, d=128, eb=2: lib.moda_append_depth_slot(  # noqa: E731
+        kv, dst, slot, B, T, L, Hk, d, eb, None)
+    assert a(kv=None) == N and a(dst=None) == N
+    assert a(slot=-1) == S and a(slot=3) == S and a(L=0) == S and a(eb=16) == S
+    assert a(kv=MIS) == AL
+
+
+def test_block_span_matches_pages_example(lib):
+    with open(os.path.join(GOLDEN, "group_rows_example.json")) as f:
+        ex = json.load(f)
+    rows = ex["rows_last"] - ex["rows_first"] + 1
+    assert api.moda_block_span(ex["rows_first"], rows, ex["G"]) == (ex["t_start"], ex["t_end"])
+    assert sorted({r // ex["G"] for r in range(ex["rows_first"], ex["rows_last"] + 1)}) == ex["base_times"]
+
+
+def test_block_span_against_brute_force(lib):
+    for G in (1, 2, 3, 4, 8, 32):
+        for row0 in range(0, 70, 7):
+            for rows in (1, 5, 32, 128):
+                ts = [r // G for r in range(row0, row0 + rows)]
+                assert api.moda_block_span(row0, rows, G) == (min(ts), max(ts) + 1)
+    with pytest.raises(api.MODAError):
+        api.moda_block_span(-1, 4, 2)
+    with pytest.raises(api.MODAError):
+        api.moda_block_span(0, 0, 2)

@@ -1,4 +1,5 @@
 """The seeded input recipe: deterministic, shaped as the workloads, shared sequence inputs."""
+import numpy as np
 import torch
 
 from depth_stream_attention_amd import inputs as I
@@ -30,9 +31,20 @@ def test_inputs_are_deterministic_and_typed():
     sh = I.Shape(1, 16, 4, 2, 8, 3)
     x = I.random_inputs(sh, 9)
     assert x["q"].dtype == torch.bfloat16
-    # bf16 values are the RNE rounding of the fp32 draw
-    g = torch.Generator("cpu").manual_seed(9)
-    assert torch.equal(x["q"], torch.randn(1, 16, 4, 8, generator=g).to(torch.bfloat16))
+    # bf16 values are the RNE rounding of the fp32 Philox draw with key = seed
+    g = np.random.Generator(np.random.Philox(key=9, counter=[0, 0, 0, 0]))
+    want = torch.from_numpy(g.standard_normal(16 * 4 * 8, dtype=np.float32)).view(1, 16, 4, 8)
+    assert torch.equal(x["q"], want.to(torch.bfloat16))
+
+
+def test_chunked_host_draw_is_thread_count_independent(monkeypatch):
+    a = I._randn((3, 1 << 21), 5)              # spans two chunks
+    monkeypatch.setattr(I.os, "cpu_count", lambda: 1)
+    b = I._randn((3, 1 << 21), 5)
+    assert torch.equal(a, b)
+    g = np.random.Generator(np.random.Philox(key=5, counter=[0, 0, 0, 1]))
+    assert torch.equal(a.reshape(-1)[1 << 22:], torch.from_numpy(g.standard_normal((3 << 21) - (1 << 22),
+                                                                                  dtype=np.float32)))
 
 
 def test_key_scale_and_empty_depth():
