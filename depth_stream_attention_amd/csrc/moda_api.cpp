@@ -18,8 +18,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool is_pow2_in(int x, int lo, int hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }
 
-int validate_fwd(const void* q, const void* k, const void* v, const void* kd, const void* vd, int B, int T, int Hq,
-                 int Hk, int d, int L, int causal, const void* out, const float* lse) {
+int validate_fwd(bool bf16, const void* q, const void* k, const void* v, const void* kd, const void* vd, int B, int T,
+                 int Hq, int Hk, int d, int L, int causal, const void* out, const float* lse) {
   if (!q || !k || !v || !out || !lse) return MODA_ERR_NULL;
   if (L > 0 && (!kd || !vd)) return MODA_ERR_NULL;
   if (B <= 0 || T <= 0 || Hq <= 0 || Hk <= 0 || d <= 0 || L < 0) return MODA_ERR_SHAPE;
@@ -31,6 +31,11 @@ int validate_fwd(const void* q, const void* k, const void* v, const void* kd, co
   // Launch-size limits of this build: expanded rows and workgroup counts in int32.
   if (static_cast<int64_t>(T) * G > INT_MAX / 2) return MODA_ERR_UNSUPPORTED;
   if (moda::fwd_bf16_grid_blocks(B, T, Hq, Hk) > INT_MAX || moda::fwd_f32_grid_blocks(B, T, Hq) > INT_MAX)
+    return MODA_ERR_UNSUPPORTED;
+  // The bf16 kernel addresses one (batch, KV head) sequence and one
+  // workgroup's depth slabs (at most 128 tokens) with 32-bit byte offsets.
+  if (bf16 && (static_cast<int64_t>(T + 64) * Hk * d * 2 >= (int64_t{1} << 31) ||
+               static_cast<int64_t>(129) * Hk * L * d * 2 >= (int64_t{1} << 31)))
     return MODA_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse)) return MODA_ERR_ALIGN;
   if (L > 0 && (!aligned16(kd) || !aligned16(vd))) return MODA_ERR_ALIGN;
@@ -49,7 +54,7 @@ int validate_layout(const void* src, const void* dst, int B, int T, int L, int H
 
 int fwd_common(bool bf16, const void* q, const void* k, const void* v, const void* kd, const void* vd, int B, int T,
                int Hq, int Hk, int d, int L, int causal, void* out, float* lse, moda_stream_t stream) {
-  const int rc = validate_fwd(q, k, v, kd, vd, B, T, Hq, Hk, d, L, causal, out, lse);
+  const int rc = validate_fwd(bf16, q, k, v, kd, vd, B, T, Hq, Hk, d, L, causal, out, lse);
   if (rc != MODA_OK) return rc;
   moda::FwdArgs a{q, k, v, L > 0 ? kd : nullptr, L > 0 ? vd : nullptr, B, T, Hq, Hk, d, L, causal, out, lse, stream};
   const hipError_t e = bf16 ? moda::launch_fwd_bf16(a) : moda::launch_fwd_f32(a);

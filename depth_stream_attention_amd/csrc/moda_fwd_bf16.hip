@@ -10,25 +10,30 @@
 //     i_q = t*G + g is token t, query head hk*G + g.  Consecutive rows of one
 //     token are its G heads, which share every K/V element they read.
 //   * A workgroup owns BM = 128 consecutive expanded rows (128/G tokens) of one
-//     (b, hk); each of its 4 waves owns 32 rows.  The block's tokens are
-//     [t_start, t_end) with t_start = floor(row0/G), t_end = floor(last/G)+1.
-//   * Sequence loop: 64-key tiles of K and V are staged in LDS once per block
-//     and read by all 4 waves.  Tiles past the block's last token are never
-//     touched; tiles that are fully visible to a wave skip the mask.
+//     (b, hk); each of its 4 waves owns 32 rows (32/G tokens).  The block's
+//     tokens are [t_start, t_end) with t_start = floor(row0/G) and
+//     t_end = floor(last/G) + 1; sequence keys at or past t_end are never read.
+//   * Every workgroup runs one pipeline of 64-row tiles staged in LDS, double
+//     buffered: while the waves compute on tile i, the global loads of tile
+//     i+1 are in flight in registers; one barrier per tile.
+//       - depth tiles come first: 16 rows per wave, 16 consecutive slots of
+//         one of the wave's own tokens, read from the packed [B][T][Hk][L][d]
+//         stream (each (token, KV head) slab is one contiguous run, each depth
+//         element is read from HBM exactly once and used by the G rows of its
+//         token only);
+//       - then the sequence tiles of 64 keys, shared by all 4 waves.
+//     Both kinds fold into the same running (max, sum, output) state of each
+//     row, so the softmax is one joint softmax over both candidate sets.
 //   * Scores are computed transposed, S^T = K * Q^T, on 32x32x16 bf16 MFMA with
 //     Q^T held in registers, so each lane owns one query row: the row max
 //     needs one cross-lane exchange (lane ^ 32) and the rescale of the output
-//     accumulator is per lane.  O^T += V^T * P^T reuses the score registers as
-//     the B operand directly; V is written to LDS transposed (d-major) with the
-//     key order permuted to match the score register layout, so every MFMA
-//     operand is one 16-byte LDS read.
-//   * Depth stage: after the sequence loop each wave stages, token by token,
-//     its own tokens' packed depth slab [L][d] (32 slots at a time) in LDS,
-//     and folds it into the SAME running (max, sum, output) state; a slot is
-//     visible only to the G rows of its token.  Each depth element is read
-//     from HBM exactly once.
-//   * Softmax runs in base 2 with log2(e)/sqrt(d) folded into one FMA; lse is
-//     converted back to the natural log at the end.
+//     accumulator is per lane.  O^T += V^T * P^T takes the score registers,
+//     packed to bf16, directly as the B operand; V is written to LDS
+//     transposed (d-major) with the key order permuted to match the score
+//     register layout, so every MFMA operand is one 16-byte LDS read.
+//   * Softmax runs in base 2 with log2(e)/sqrt(d) folded into the exponent's
+//     FMA; the output rescale is skipped when no row max of the wave moved.
+//     lse is converted back to the natural log at the end.
 //   * Causal workgroups are issued heaviest first (last row block first).
 #include "moda_device.h"
 #include "moda_launch.h"
@@ -40,22 +45,17 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kRowsPerWave = 32;
 constexpr int kBM = kWaves * kRowsPerWave;  // expanded rows per workgroup
-constexpr int kBN = 64;                     // sequence keys per tile
-constexpr int kBD = 32;                     // depth slots per depth tile
+constexpr int kBN = 64;                     // rows (keys or depth slots) per tile
+constexpr int kDepthRowsPerWave = kBN / kWaves;
 
 template <int D>
 struct Smem {
-  static constexpr int KS = D + 8;     // K row stride (elements): +16 B breaks bank aliasing
-  static constexpr int VS = kBN + 8;   // V^T row stride for sequence tiles
-  static constexpr int VSD = kBD + 8;  // V^T row stride for depth tiles
-  static constexpr int kSeqK = kBN * KS;
-  static constexpr int kSeqV = D * VS;
-  static constexpr int kDepK = kBD * KS;
-  static constexpr int kDepV = D * VSD;
-  static constexpr int kDepWave = kDepK + kDepV;
-  static constexpr int kSeqTotal = kSeqK + kSeqV;
-  static constexpr int kDepTotal = kWaves * kDepWave;
-  static constexpr int kElems = kSeqTotal > kDepTotal ? kSeqTotal : kDepTotal;
+  static constexpr int KS = D + 8;    // K row stride (elements): +16 B breaks bank aliasing
+  static constexpr int VS = kBN + 8;  // V^T row stride
+  static constexpr int kK = kBN * KS;
+  static constexpr int kV = D * VS;
+  static constexpr int kBuf = kK + kV;
+  static constexpr int kElems = 2 * kBuf;
 };
 
 // Position of tile key `kk` inside a d-row of the transposed V tile.  Within
@@ -67,31 +67,100 @@ __device__ __forceinline__ int vpos(int kk) {
   return (kk & ~15) | (bb << 3) | (a << 2) | (kk & 3);
 }
 
-// Stage `nrows` rows (keys or slots) of K as row-major [row][d] and of V as
-// transposed [d][vpos(row)], zero-filling rows >= valid.  Row r of K (V) is
-// at kg + r*stride (vg + r*stride).  Threads [t0, t0 + nthr) take part.
-template <int D, int NROWS, int VSTRIDE>
-__device__ __forceinline__ void stage_kv(const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
-                                         int64_t stride, int valid, uint16_t* ks, uint16_t* vt,
-                                         int tid, int nthr) {
-  constexpr int KS = D + 8;
-  constexpr int CH = D / 8;  // 16-byte chunks per row
-  for (int c = tid; c < NROWS * CH; c += nthr) {
-    const int row = c / CH, ch = c % CH;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (row < valid) val = *reinterpret_cast<const u32x4*>(kg + row * stride + ch * 8);
-    *reinterpret_cast<u32x4*>(ks + row * KS + ch * 8) = val;
-  }
-  for (int it = tid; it < (NROWS / 4) * CH; it += nthr) {
-    const int quad = it % (NROWS / 4), oc = it / (NROWS / 4);
-    u32x4 r[4];
+// Per-workgroup staging geometry.  All global tile reads are raw buffer loads
+// against four descriptors whose ranges end exactly at the last valid row, so
+// rows past the end of the sequence read as zero; padding depth slots (slot
+// >= L) get an offset beyond every range and read as zero too.
+//   seq K/V : base &x[b][0][hk][0], key j at byte j * Hk*d*2.
+//   depth   : base &x[b][t_b][hk][0][0] with t_b the workgroup's first token;
+//             token t_b + u, slot i at byte (u*Hk*L + i) * d*2.
+struct Geo {
+  __amdgpu_buffer_rsrc_t k, v, kd, vd;
+  int L;
+  uint32_t key_bytes;   // Hk*d*2: stride between consecutive keys of one KV head
+  uint32_t tok_bytes;   // Hk*L*d*2: stride between consecutive tokens' depth slabs
+  int tok_wave;         // tokens per wave (32 / G)
+};
+
+constexpr uint32_t kOutOfRange = 0x80000000u;  // > every descriptor range (host-checked)
+constexpr int kBufFlags = 0x00020000;         // raw buffer, 32-bit dwords
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint16_t* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), kBufFlags);
+}
+
+// Byte offset of 16-byte column chunk `ch` of tile row r at pipeline step it.
+// Steps [0, nd) are depth tiles: for every wave w, token w*tok_wave + dtok of
+// the workgroup and slots [16*dch, 16*dch + 16), at tile rows [16w, 16w + 16).
+// Steps >= nd are sequence tiles of 64 keys starting at kt0.
+template <int D>
+__device__ __forceinline__ uint32_t tile_row_bytes(const Geo& g, bool depth, int kt0, int dtok, int dch, int r,
+                                                   int ch) {
+  if (!depth) return static_cast<uint32_t>(kt0 + r) * g.key_bytes + ch * 16;
+  const int w = r / kDepthRowsPerWave;
+  const int slot = dch * kDepthRowsPerWave + (r % kDepthRowsPerWave);
+  if (slot >= g.L) return kOutOfRange;
+  return static_cast<uint32_t>(w * g.tok_wave + dtok) * g.tok_bytes + static_cast<uint32_t>(slot) * (D * 2) +
+         ch * 16;
+}
+
+// Register staging of one tile: each thread holds up to KCH 16-byte K chunks
+// and one (4-row, 8-column) V block per VIT item.
+template <int D>
+struct Stage {
+  static constexpr int CH = D / 8;                                  // 16-byte chunks per row
+  static constexpr int KCH = (kBN * CH + kThreads - 1) / kThreads;  // K chunks per thread
+  static constexpr int VIT = ((kBN / 4) * CH + kThreads - 1) / kThreads;
+  u32x4 kc[KCH];
+  u32x4 vr[VIT][4];
+};
+
+template <int D, bool DEPTH_TILE>
+__device__ __forceinline__ void load_tile(Stage<D>& s, const Geo& g, int it, int nd, int nchunk, int tid) {
+  constexpr int CH = Stage<D>::CH;
+  constexpr bool depth = DEPTH_TILE;
+  const int dtok = depth ? it / nchunk : 0;
+  const int dch = depth ? it - dtok * nchunk : 0;
+  const int kt0 = depth ? 0 : (it - nd) * kBN;
+  const __amdgpu_buffer_rsrc_t rk = depth ? g.kd : g.k;
+  const __amdgpu_buffer_rsrc_t rv = depth ? g.vd : g.v;
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const int row = quad * 4 + x;
-      r[x] = u32x4{0u, 0u, 0u, 0u};
-      if (row < valid) r[x] = *reinterpret_cast<const u32x4*>(vg + row * stride + oc * 8);
+  for (int x = 0; x < Stage<D>::KCH; ++x) {
+    const int c = tid + x * kThreads;
+    uint32_t off = kOutOfRange;
+    if (c < kBN * CH) off = tile_row_bytes<D>(g, depth, kt0, dtok, dch, c / CH, c % CH);
+    s.kc[x] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+  }
+#pragma unroll
+  for (int x = 0; x < Stage<D>::VIT; ++x) {
+    const int item = tid + x * kThreads;
+    const int quad = item % (kBN / 4), oc = item / (kBN / 4);
+#pragma unroll
+    for (int y = 0; y < 4; ++y) {
+      uint32_t off = kOutOfRange;
+      if (item < (kBN / 4) * CH) off = tile_row_bytes<D>(g, depth, kt0, dtok, dch, quad * 4 + y, oc);
+      s.vr[x][y] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
     }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_tile(const Stage<D>& s, uint16_t* ks, uint16_t* vt, int tid) {
+  constexpr int CH = Stage<D>::CH;
+  constexpr int KS = Smem<D>::KS, VS = Smem<D>::VS;
+#pragma unroll
+  for (int x = 0; x < Stage<D>::KCH; ++x) {
+    const int c = tid + x * kThreads;
+    if (c < kBN * CH) *reinterpret_cast<u32x4*>(ks + (c / CH) * KS + (c % CH) * 8) = s.kc[x];
+  }
+#pragma unroll
+  for (int x = 0; x < Stage<D>::VIT; ++x) {
+    const int item = tid + x * kThreads;
+    if (item >= (kBN / 4) * CH) continue;
+    const int quad = item % (kBN / 4), oc = item / (kBN / 4);
     const int pos = vpos(quad * 4);
+    const u32x4* r = s.vr[x];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int w = e >> 1;
@@ -103,7 +172,7 @@ __device__ __forceinline__ void stage_kv(const uint16_t* __restrict__ kg, const 
         lo = (r[0][w] & 0xffffu) | (r[1][w] << 16);
         hi = (r[2][w] & 0xffffu) | (r[3][w] << 16);
       }
-      *reinterpret_cast<u32x2*>(vt + (oc * 8 + e) * VSTRIDE + pos) = u32x2{lo, hi};
+      *reinterpret_cast<u32x2*>(vt + (oc * 8 + e) * VS + pos) = u32x2{lo, hi};
     }
   }
 }
@@ -116,58 +185,46 @@ struct RowState {
   float l;           // this lane's share of the running denominator
 };
 
-// Fold one 32-key block of scores (already scaled to base 2, -inf = masked)
-// into the state.  x[i] belongs to key 8*(i/4) + 4*half + (i%4) of the block.
-// Returns the unnormalised weights, packed to bf16, as the two B operands of
-// the PV product (keys 0..15 and 16..31 of the block).
-template <int D>
-__device__ __forceinline__ void online_update(RowState<D>& st, float (&x)[16], bf16x8 (&pb)[2]) {
-  float mx = x[0];
+// Fold N raw scores (-inf = masked) into the state and return the weights,
+// packed to bf16 in groups of 8 (one PV B operand per group).
+template <int D, int N>
+__device__ __forceinline__ void online_update(RowState<D>& st, float (&s)[N], bf16x8 (&pb)[N / 8], float scale) {
+  float mx = s[0];
 #pragma unroll
-  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
+  for (int i = 1; i < N; ++i) mx = fmaxf(mx, s[i]);
   mx = fmaxf(mx, wave_xor32(mx));
-  const float m_new = fmaxf(st.m, mx);
+  const float m_new = fmaxf(st.m, mx * scale);  // -inf stays -inf (scale > 0)
   const float base = (m_new == -INFINITY) ? 0.0f : m_new;
-  const float alpha = fast_exp2(st.m - base);
+  if (__any(m_new != st.m)) {
+    const float alpha = fast_exp2(st.m - base);
+    st.l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st.o[dt][i] *= alpha;
+  }
+  st.m = m_new;
   float sum = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    x[i] = fast_exp2(x[i] - base);
-    sum += x[i];
+  for (int i = 0; i < N; ++i) {
+    s[i] = fast_exp2(fmaf(s[i], scale, -base));
+    sum += s[i];
   }
-  st.l = st.l * alpha + sum;
-  st.m = m_new;
+  st.l += sum;
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) st.o[dt][i] *= alpha;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < N / 8; ++h) {
     u32x4 w;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) w[k] = pack_bf16x2(x[8 * h + 2 * k], x[8 * h + 2 * k + 1]);
+    for (int k = 0; k < 4; ++k) w[k] = pack_bf16x2(s[8 * h + 2 * k], s[8 * h + 2 * k + 1]);
     pb[h] = __builtin_bit_cast(bf16x8, w);
   }
 }
 
-// O^T += V^T * P^T for one 32-key block (two 16-key products per d tile).
-template <int D, int VSTRIDE>
-__device__ __forceinline__ void pv_block(RowState<D>& st, const bf16x8 (&pb)[2], const uint16_t* vt,
-                                         int key0, int r, int half) {
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(vt + (dt * 32 + r) * VSTRIDE + key0 + 16 * h + 8 * half);
-      st.o[dt] = mfma32(a, pb[h], st.o[dt]);
-    }
-}
-
-// S^T block: 32 keys (rows of ks starting at key0) x 32 query rows.
+// S^T block: 32 keys (rows of ks starting at key0) x the wave's 32 query rows.
 template <int D>
 __device__ __forceinline__ f32x16 qk_block(const bf16x8 (&qf)[D / 16], const uint16_t* ks, int key0, int r,
                                            int half) {
-  constexpr int KS = D + 8;
+  constexpr int KS = Smem<D>::KS;
   f32x16 s = {};
 #pragma unroll
   for (int sl = 0; sl < D / 16; ++sl) {
@@ -175,6 +232,18 @@ __device__ __forceinline__ f32x16 qk_block(const bf16x8 (&qf)[D / 16], const uin
     s = mfma32(a, qf[sl], s);
   }
   return s;
+}
+
+// O^T += V^T * P^T for one 16-key group starting at tile key key0 + 16*h.
+template <int D>
+__device__ __forceinline__ void pv_group(RowState<D>& st, const bf16x8& pb, const uint16_t* vt, int key16, int r,
+                                         int half) {
+  constexpr int VS = Smem<D>::VS;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(vt + (dt * 32 + r) * VS + key16 + 8 * half);
+    st.o[dt] = mfma32(a, pb, st.o[dt]);
+  }
 }
 
 template <int D, bool DEPTH, bool CAUSAL>
@@ -192,20 +261,49 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int bid = blockIdx.x;
   const int rb = CAUSAL ? (nrb - 1 - bid / nbh) : (bid / nbh);
   const int bh = bid % nbh;
+
   const int b = bh / Hk, hk = bh % Hk;
-  const int TG = T << lgG;
   const int row0 = rb * kBM;
+  const int TG = T << lgG;
+  const int tb = row0 >> lgG;  // the workgroup's first token
+
+  Geo g;
+  g.L = DEPTH ? L : 0;
+  g.tok_wave = (kRowsPerWave >> lgG) > 0 ? (kRowsPerWave >> lgG) : 1;
+  g.key_bytes = static_cast<uint32_t>(Hk) * D * 2;
+  g.tok_bytes = static_cast<uint32_t>(Hk) * (DEPTH ? L : 0) * D * 2;
+  {
+    const uint16_t* kb = k + (static_cast<int64_t>(b) * T * Hk + hk) * D;
+    const uint16_t* vb = v + (static_cast<int64_t>(b) * T * Hk + hk) * D;
+    const uint32_t seq_range = (static_cast<uint32_t>(T - 1) * Hk + 1) * D * 2;
+    g.k = make_rsrc(kb, seq_range);
+    g.v = make_rsrc(vb, seq_range);
+    if (DEPTH) {
+      const int64_t slab0 = ((static_cast<int64_t>(b) * T + tb) * Hk + hk) * static_cast<int64_t>(L) * D;
+      const int64_t range = ((static_cast<int64_t>(T - 1 - tb) * Hk + 1) * L) * D * 2;
+      const uint32_t dr = static_cast<uint32_t>(range < 0x7fffffff ? range : 0x7fffffff);
+      g.kd = make_rsrc(kd + slab0, dr);
+      g.vd = make_rsrc(vd + slab0, dr);
+    } else {
+      g.kd = g.k;
+      g.vd = g.v;
+    }
+  }
+
   const int wrow0 = row0 + wave * kRowsPerWave;
   const int my_row = wrow0 + r;
   const bool row_ok = my_row < TG;
   const int my_t = my_row >> lgG;
   const int my_g = my_row & (G - 1);
   const bool wave_live = wrow0 < TG;
-  const int wt0 = wrow0 >> lgG;                                        // wave's first token
-  const int wt1 = (min(wrow0 + kRowsPerWave, TG) - 1) >> lgG;          // wave's last valid token
-  const int blk_last = (min(row0 + kBM, TG) - 1) >> lgG;               // block's last valid token
+  const int wt0 = wrow0 >> lgG;                                    // wave's first token
+  const int wt1 = (min(wrow0 + kRowsPerWave, TG) - 1) >> lgG;      // wave's last valid token
+  const int blk_last = (min(row0 + kBM, TG) - 1) >> lgG;           // block's last valid token
   const int kv_end = CAUSAL ? blk_last + 1 : T;
-  const int ntiles = (kv_end + kBN - 1) / kBN;
+  const int ns = (kv_end + kBN - 1) / kBN;                         // sequence tiles
+  const int nchunk = DEPTH ? (L + kDepthRowsPerWave - 1) / kDepthRowsPerWave : 1;  // 16-slot chunks per token
+  const int nd = DEPTH ? g.tok_wave * nchunk : 0;                                  // depth tiles
+  const int ntot = nd + ns;
 
   // Q^T fragments (B operand): lane holds row my_row, d = 16*sl + 8*half + [0, 8).
   bf16x8 qf[D / 16];
@@ -225,69 +323,73 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   st.m = -INFINITY;
   st.l = 0.0f;
 
-  const int64_t kv_stride = static_cast<int64_t>(Hk) * D;
-  const uint16_t* kbase = k + (static_cast<int64_t>(b) * T * Hk + hk) * D;
-  const uint16_t* vbase = v + (static_cast<int64_t>(b) * T * Hk + hk) * D;
-  uint16_t* ks = smem;
-  uint16_t* vt = smem + S::kSeqK;
+  // In depth tile it this wave's 16 rows (token wt0 + it / nchunk, slots from
+  // 16 * (it % nchunk)) sit at tile rows [16*wave, 16*wave + 16): 32-key block
+  // wave/2, score registers [8*(wave%2), 8*(wave%2) + 8).
+  const int dj = wave >> 1, dh = wave & 1;
 
-  // ---- sequence loop -------------------------------------------------------
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const int kt0 = tile * kBN;
-    __syncthreads();
-    stage_kv<D, kBN, S::VS>(kbase + kt0 * kv_stride, vbase + kt0 * kv_stride, kv_stride, min(kBN, T - kt0), ks,
-                           vt, tid, kThreads);
-    __syncthreads();
-    if (!wave_live || (CAUSAL && kt0 > wt1)) continue;  // nothing visible to this wave
-    const bool need_mask = (kt0 + kBN > T) || (CAUSAL && kt0 + kBN - 1 > wt0);
+  Stage<D> stage;
+  if (nd > 0)
+    load_tile<D, true>(stage, g, 0, nd, nchunk, tid);
+  else
+    load_tile<D, false>(stage, g, 0, nd, nchunk, tid);
+
+  // ---- depth tiles: each wave sees only its own token's slots ----------------
+  if constexpr (DEPTH) {
+    for (int it = 0; it < nd; ++it) {
+      uint16_t* ks = smem + (it & 1) * S::kBuf;
+      uint16_t* vt = ks + S::kK;
+      store_tile<D>(stage, ks, vt, tid);
+      __syncthreads();
+      if (it + 1 < nd)
+        load_tile<D, true>(stage, g, it + 1, nd, nchunk, tid);
+      else if (ns > 0)
+        load_tile<D, false>(stage, g, it + 1, nd, nchunk, tid);
+      if (!wave_live) continue;
+      const f32x16 sacc = qk_block<D>(qf, ks, 32 * dj, r, half);
+      const int dtok = it / nchunk;
+      const int slot0 = (it - dtok * nchunk) * kDepthRowsPerWave;
+      const bool mine = my_t == wt0 + dtok;
+      float s[8];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      f32x16 s = qk_block<D>(qf, ks, 32 * j, r, half);
-      float x[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        x[i] = s[i] * scale_log2;
-        if (need_mask) {
-          const int key = kt0 + 32 * j + 8 * (i >> 2) + 4 * half + (i & 3);
-          const bool vis = key < T && (!CAUSAL || key <= my_t);
-          if (!vis) x[i] = -INFINITY;
-        }
+      for (int i = 0; i < 8; ++i) {
+        const int slot = slot0 + 8 * (i >> 2) + 4 * half + (i & 3);
+        s[i] = (mine && slot < L) ? sacc[8 * dh + i] : -INFINITY;
       }
-      bf16x8 pb[2];
-      online_update<D>(st, x, pb);
-      pv_block<D, S::VS>(st, pb, vt, 32 * j, r, half);
+      bf16x8 pb[1];
+      online_update<D, 8>(st, s, pb, scale_log2);
+      pv_group<D>(st, pb[0], vt, 32 * dj + 16 * dh, r, half);
     }
   }
 
-  // ---- depth stage ---------------------------------------------------------
-  if constexpr (DEPTH) {
-    const int tok_per_wave = (kRowsPerWave >> lgG) > 0 ? (kRowsPerWave >> lgG) : 1;
-    const int nchunks = (L + kBD - 1) / kBD;
-    uint16_t* kds = smem + wave * S::kDepWave;
-    uint16_t* vdt = kds + S::kDepK;
-    for (int kt = 0; kt < tok_per_wave; ++kt) {
-      const int tw = wt0 + kt;  // this wave's token for this step
-      const bool tok_ok = wave_live && tw < T && tw <= wt1;
-      const int64_t slab = ((static_cast<int64_t>(b) * T + (tok_ok ? tw : 0)) * Hk + hk) * L;
-      for (int ch = 0; ch < nchunks; ++ch) {
-        const int i0 = ch * kBD;
-        __syncthreads();
-        const int valid = tok_ok ? min(kBD, L - i0) : 0;
-        stage_kv<D, kBD, S::VSD>(kd + (slab + i0) * D, vd + (slab + i0) * D, D, valid, kds, vdt, lane, 64);
-        __syncthreads();
-        if (!tok_ok) continue;
-        f32x16 s = qk_block<D>(qf, kds, 0, r, half);
-        float x[16];
+  // ---- sequence tiles ----------------------------------------------------------
+  for (int it = nd; it < ntot; ++it) {
+    uint16_t* ks = smem + (it & 1) * S::kBuf;
+    uint16_t* vt = ks + S::kK;
+    store_tile<D>(stage, ks, vt, tid);
+    __syncthreads();
+    if (it + 1 < ntot) load_tile<D, false>(stage, g, it + 1, nd, nchunk, tid);
+    if (!wave_live) continue;
+    const int kt0 = (it - nd) * kBN;
+    if (CAUSAL && kt0 > wt1) continue;  // nothing visible to this wave
+    const bool need_mask = (kt0 + kBN > T) || (CAUSAL && kt0 + kBN - 1 > wt0);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int slot = i0 + 8 * (i >> 2) + 4 * half + (i & 3);
-          const bool vis = (my_t == tw) && slot < L;
-          x[i] = vis ? s[i] * scale_log2 : -INFINITY;
+    for (int j = 0; j < 2; ++j) {
+      const f32x16 sacc = qk_block<D>(qf, ks, 32 * j, r, half);
+      float s[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        s[i] = sacc[i];
+        if (need_mask) {
+          const int key = kt0 + 32 * j + 8 * (i >> 2) + 4 * half + (i & 3);
+          const bool vis = key < T && (!CAUSAL || key <= my_t);
+          if (!vis) s[i] = -INFINITY;
         }
-        bf16x8 pb[2];
-        online_update<D>(st, x, pb);
-        pv_block<D, S::VSD>(st, pb, vdt, 0, r, half);
       }
+      bf16x8 pb[2];
+      online_update<D, 16>(st, s, pb, scale_log2);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) pv_group<D>(st, pb[h], vt, 32 * j + 16 * h, r, half);
     }
   }
 

@@ -57,6 +57,9 @@ def test_fwd_validation(lib, name):
         assert f(**kw) == AL, kw
     assert f(kd=MIS, vd=MIS, L=0) != AL                # depth pointers are ignored when L == 0
     assert f(T=(1 << 30), Hq=32, Hk=1) == U            # expanded rows beyond int32 launch limits
+    if name == "moda_attn_fwd":                        # 32-bit buffer offsets of the bf16 kernel
+        assert f(T=(1 << 22), Hq=16, Hk=8) == U
+        assert f(L=1024, Hq=64, Hk=64) == U
 
 
 def test_layout_validation(lib):
