@@ -31,6 +31,24 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
+// Lanes l and l ^ 32 exchange through v_permlane32_swap (upper half of the
+// first operand <-> lower half of the second).  With both operands holding x,
+// afterwards each lane has x[l] in one and x[l ^ 32] in the other, so their
+// max / sum needs no select.  Issued as inline asm: the compiler builtin,
+// given two equal inputs, folds its two results into one.  The leading
+// s_nop covers the VALU-write -> permlane-read hazard.
+__device__ __forceinline__ void swap_halves(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float pair_max(float x) {
+  float a = x, b = x;
+  swap_halves(a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  float a = x, b = x;
+  swap_halves(a, b);
+  return a + b;
+}
 
 }  // namespace moda

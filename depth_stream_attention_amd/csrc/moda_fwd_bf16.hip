@@ -181,9 +181,15 @@ __device__ __forceinline__ void store_tile(const Stage<D>& s, uint16_t* ks, uint
 template <int D>
 struct RowState {
   f32x16 o[D / 32];  // O^T accumulator: d = 32*dt + 8*(i/4) + 4*half + (i%4)
-  float m;           // running max of the base-2 scaled logits (same in both lanes)
+  float m;           // base-2 exponent offset of the row (same in both lanes)
   float l;           // this lane's share of the running denominator
 };
+
+// The row's exponent offset m only moves when a block's max exceeds it by more
+// than this (base 2), so unnormalised weights stay below 2^8 and the costly
+// rescale of the output accumulator is rare.  Any offset gives the same
+// quotient; the final division and lse use the offset actually applied.
+constexpr float kRescaleSlack = 8.0f;
 
 // Fold N raw scores (-inf = masked) into the state and return the weights,
 // packed to bf16 in groups of 8 (one PV B operand per group).
@@ -192,18 +198,19 @@ __device__ __forceinline__ void online_update(RowState<D>& st, float (&s)[N], bf
   float mx = s[0];
 #pragma unroll
   for (int i = 1; i < N; ++i) mx = fmaxf(mx, s[i]);
-  mx = fmaxf(mx, wave_xor32(mx));
-  const float m_new = fmaxf(st.m, mx * scale);  // -inf stays -inf (scale > 0)
-  const float base = (m_new == -INFINITY) ? 0.0f : m_new;
-  if (__any(m_new != st.m)) {
-    const float alpha = fast_exp2(st.m - base);
+  mx = pair_max(mx);
+  const float m_blk = mx * scale;  // -inf stays -inf (scale > 0)
+  if (__any(m_blk > st.m + kRescaleSlack)) {
+    const float m_new = fmaxf(st.m, m_blk);
+    const float alpha = fast_exp2(st.m - (m_new == -INFINITY ? 0.0f : m_new));
     st.l *= alpha;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) st.o[dt][i] *= alpha;
+    st.m = m_new;
   }
-  st.m = m_new;
+  const float base = (st.m == -INFINITY) ? 0.0f : st.m;
   float sum = 0.0f;
 #pragma unroll
   for (int i = 0; i < N; ++i) {
@@ -246,6 +253,33 @@ __device__ __forceinline__ void pv_group(RowState<D>& st, const bf16x8& pb, cons
   }
 }
 
+// One 64-key sequence tile: two 32-key blocks of S^T, each folded into the
+// state and multiplied into O^T.  MASK applies the causal / sequence-end mask
+// (branch-free selects); interior tiles take the MASK = false path.
+template <int D, bool MASK, bool CAUSAL>
+__device__ __forceinline__ void seq_tile(RowState<D>& st, const bf16x8 (&qf)[D / 16], const uint16_t* ks,
+                                         const uint16_t* vt, int kt0, int T, int my_t, int r, int half,
+                                         float scale) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const f32x16 sacc = qk_block<D>(qf, ks, 32 * j, r, half);
+    float s[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      s[i] = sacc[i];
+      if (MASK) {
+        const int key = kt0 + 32 * j + 8 * (i >> 2) + 4 * half + (i & 3);
+        const bool vis = key < T && (!CAUSAL || key <= my_t);
+        s[i] = vis ? s[i] : -INFINITY;
+      }
+    }
+    bf16x8 pb[2];
+    online_update<D, 16>(st, s, pb, scale);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) pv_group<D>(st, pb[h], vt, 32 * j + 16 * h, r, half);
+  }
+}
+
 template <int D, bool DEPTH, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void moda_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -255,7 +289,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   __shared__ __attribute__((aligned(16))) uint16_t smem[S::kElems];
 
   const int G = 1 << lgG;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps per-wave control scalar
   const int r = lane & 31, half = lane >> 5;
   const int nbh = B * Hk;
   const int bid = blockIdx.x;
@@ -295,7 +330,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const bool row_ok = my_row < TG;
   const int my_t = my_row >> lgG;
   const int my_g = my_row & (G - 1);
-  const bool wave_live = wrow0 < TG;
   const int wt0 = wrow0 >> lgG;                                    // wave's first token
   const int wt1 = (min(wrow0 + kRowsPerWave, TG) - 1) >> lgG;      // wave's last valid token
   const int blk_last = (min(row0 + kBM, TG) - 1) >> lgG;           // block's last valid token
@@ -345,7 +379,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         load_tile<D, true>(stage, g, it + 1, nd, nchunk, tid);
       else if (ns > 0)
         load_tile<D, false>(stage, g, it + 1, nd, nchunk, tid);
-      if (!wave_live) continue;
       const f32x16 sacc = qk_block<D>(qf, ks, 32 * dj, r, half);
       const int dtok = it / nchunk;
       const int slot0 = (it - dtok * nchunk) * kDepthRowsPerWave;
@@ -363,38 +396,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
 
   // ---- sequence tiles ----------------------------------------------------------
-  for (int it = nd; it < ntot; ++it) {
+  // Tiles wholly before the workgroup's first token and the sequence end are
+  // unmasked for every wave: one straight-line loop with no per-wave control
+  // flow (so the accumulator keeps its registers).  The remaining few tiles
+  // overlap the workgroup's own tokens and take the masked path.
+  const int tb_first = row0 >> lgG;
+  const int n_int = CAUSAL ? min(ns, (tb_first + 1) / kBN) : T / kBN;
+  for (int it = nd; it < nd + n_int; ++it) {
     uint16_t* ks = smem + (it & 1) * S::kBuf;
     uint16_t* vt = ks + S::kK;
     store_tile<D>(stage, ks, vt, tid);
     __syncthreads();
     if (it + 1 < ntot) load_tile<D, false>(stage, g, it + 1, nd, nchunk, tid);
-    if (!wave_live) continue;
+    seq_tile<D, false, CAUSAL>(st, qf, ks, vt, (it - nd) * kBN, T, my_t, r, half, scale_log2);
+  }
+  for (int it = nd + n_int; it < ntot; ++it) {
+    uint16_t* ks = smem + (it & 1) * S::kBuf;
+    uint16_t* vt = ks + S::kK;
+    store_tile<D>(stage, ks, vt, tid);
+    __syncthreads();
+    if (it + 1 < ntot) load_tile<D, false>(stage, g, it + 1, nd, nchunk, tid);
     const int kt0 = (it - nd) * kBN;
     if (CAUSAL && kt0 > wt1) continue;  // nothing visible to this wave
-    const bool need_mask = (kt0 + kBN > T) || (CAUSAL && kt0 + kBN - 1 > wt0);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const f32x16 sacc = qk_block<D>(qf, ks, 32 * j, r, half);
-      float s[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        s[i] = sacc[i];
-        if (need_mask) {
-          const int key = kt0 + 32 * j + 8 * (i >> 2) + 4 * half + (i & 3);
-          const bool vis = key < T && (!CAUSAL || key <= my_t);
-          if (!vis) s[i] = -INFINITY;
-        }
-      }
-      bf16x8 pb[2];
-      online_update<D, 16>(st, s, pb, scale_log2);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) pv_group<D>(st, pb[h], vt, 32 * j + 16 * h, r, half);
-    }
+    seq_tile<D, true, CAUSAL>(st, qf, ks, vt, kt0, T, my_t, r, half, scale_log2);
   }
 
   // ---- epilogue --------------------------------------------------------------
-  const float l_tot = st.l + wave_xor32(st.l);
+  const float l_tot = pair_sum(st.l);
   if (row_ok) {
     const float inv = 1.0f / l_tot;
     const int h = hk * G + my_g;
