@@ -86,6 +86,77 @@ def cpu_baseline(shape, host, budget_s):
     return rec, np.concatenate(rows_all), np.concatenate(ref_all)
 
 
+def _read_csv(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _kernel_label(name):
+    if "moda_fwd_bf16_kernel" in name:
+        depth = name.split("<")[1].split(",")[1].strip()
+        return "moda_fwd_bf16 L=48" if depth == "true" else "moda_fwd_bf16 L=0"
+    if "pack_kernel" in name:
+        return "moda_pack_depth"
+    return None
+
+
+def summarize(trace_dir, fetch_dir, write_dir, command):
+    """Turn rocprofv3 CSVs of this benchmark into the committed summary and traffic record.
+
+    FETCH_SIZE / WRITE_SIZE are calibrated on the depth packer, a plain copy kernel of known
+    size (it reads and writes 2*B*T*L*Hk*d bytes per launch)."""
+    shape = I.workload(5, 0)
+    pack_bytes = acc.depth_bytes(shape) / 2  # one of K / V
+    stats = {}
+    for r in _read_csv(os.path.join(trace_dir, "run_kernel_stats.csv")):
+        lab = _kernel_label(r["Name"])
+        if lab:
+            stats[lab] = (int(r["Calls"]), float(r["AverageNs"]) / 1e6, float(r["MinNs"]) / 1e6,
+                          float(r["MaxNs"]) / 1e6)
+    counters = {}
+    for d, cname in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
+        vals = {}
+        for r in _read_csv(os.path.join(d, "run_counter_collection.csv")):
+            lab = _kernel_label(r["Kernel_Name"])
+            if lab and r["Counter_Name"] == cname:
+                vals.setdefault(lab, []).append(float(r["Counter_Value"]) * 1024.0)  # KiB -> bytes
+        counters[cname] = {k: float(np.mean(v)) for k, v in vals.items()}
+    f_scale = pack_bytes / counters["FETCH_SIZE"]["moda_pack_depth"]
+    w_scale = pack_bytes / counters["WRITE_SIZE"]["moda_pack_depth"]
+    lines = ["# rocprofv3 summary: MoDA forward, long-context layer B=1 T=65536 Hq=16 Hk=4 d=128, bf16",
+             "", "kernel trace (rocprofv3 --kernel-trace --stats):", "  command: " + command[0], "",
+             "  %-22s %6s %12s %12s %12s" % ("kernel", "calls", "avg ms", "min ms", "max ms")]
+    for lab, (n, avg, mn, mx) in sorted(stats.items()):
+        lines.append("  %-22s %6d %12.4f %12.4f %12.4f" % (lab, n, avg, mn, mx))
+    F = acc.flops(shape)
+    F0 = acc.flops(I.workload(5, 1))
+    avg48, avg0 = stats["moda_fwd_bf16 L=48"][1], stats["moda_fwd_bf16 L=0"][1]
+    lines += ["", "  MoDA L=48: %.1f TFLOP/s (%.4g flop / %.4f ms); L=0: %.1f TFLOP/s; ratio %.4f" % (
+        F / avg48 / 1e9, F, avg48, F0 / avg0 / 1e9, avg48 / avg0), "",
+        "HBM traffic per launch (rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE, separate runs):",
+        "  commands: " + command[1], "            " + command[2],
+        "  calibration on moda_pack_depth (reads and writes %d bytes): FETCH_SIZE x %.4f, WRITE_SIZE x %.4f"
+        % (pack_bytes, f_scale, w_scale), ""]
+    traffic = {}
+    for lab in ("moda_fwd_bf16 L=48", "moda_fwd_bf16 L=0", "moda_pack_depth"):
+        rd = counters["FETCH_SIZE"].get(lab, 0.0) * f_scale
+        wr = counters["WRITE_SIZE"].get(lab, 0.0) * w_scale
+        traffic[lab] = rd + wr
+        lines.append("  %-22s read %.4g B  write %.4g B  total %.4g B" % (lab, rd, wr, rd + wr))
+    alg = acc.algorithmic_bytes(shape)
+    lines.append("  algorithmic bytes of the L=48 forward: %.4g B (traffic / algorithmic = %.3f)"
+                 % (alg, traffic["moda_fwd_bf16 L=48"] / alg))
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(os.path.join(os.path.dirname(TRAFFIC_FILE), "moda_fwd_bf16_long_L48.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump({"kernel": "moda_fwd_bf16 L=48", "kernel_source_hash": kernel_source_hash(),
+                   "hbm_bytes_per_launch": traffic["moda_fwd_bf16 L=48"],
+                   "fetch_scale": f_scale, "write_scale": w_scale}, f, indent=1)
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -93,7 +164,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write the profiles/ summary from rocprofv3 CSV output directories and exit")
+    ap.add_argument("--commands", nargs=3, default=["", "", ""], help="the three rocprofv3 commands, for the record")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(*args.summarize, command=args.commands)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: the MoDA forward has no multi-GPU path here (each (batch, KV head) "
               "unit is independent; see the sharding notes). Run with --gpus 1.", file=sys.stderr)

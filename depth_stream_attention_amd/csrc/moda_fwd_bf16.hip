@@ -15,13 +15,13 @@
 //     t_end = floor(last/G) + 1; sequence keys at or past t_end are never read.
 //   * Every workgroup runs one pipeline of 64-row tiles staged in LDS, double
 //     buffered: while the waves compute on tile i, the global loads of tile
-//     i+1 are in flight in registers; one barrier per tile.
-//       - depth tiles come first: 16 rows per wave, 16 consecutive slots of
-//         one of the wave's own tokens, read from the packed [B][T][Hk][L][d]
-//         stream (each (token, KV head) slab is one contiguous run, each depth
+//     i+1 are in flight in registers; one barrier per tile.  Two kinds:
+//       - sequence tiles of 64 keys, shared by all 4 waves;
+//       - depth tiles: 16 rows per wave, 16 consecutive slots of one of the
+//         wave's own tokens, read from the packed [B][T][Hk][L][d] stream
+//         (each (token, KV head) slab is one contiguous run, each depth
 //         element is read from HBM exactly once and used by the G rows of its
-//         token only);
-//       - then the sequence tiles of 64 keys, shared by all 4 waves.
+//         token only), spread evenly among the sequence tiles.
 //     Both kinds fold into the same running (max, sum, output) state of each
 //     row, so the softmax is one joint softmax over both candidate sets.
 //   * Scores are computed transposed, S^T = K * Q^T, on 32x32x16 bf16 MFMA with
@@ -90,19 +90,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint16_t* base
                                            static_cast<int>(bytes), kBufFlags);
 }
 
-// Byte offset of 16-byte column chunk `ch` of tile row r at pipeline step it.
-// Steps [0, nd) are depth tiles: for every wave w, token w*tok_wave + dtok of
-// the workgroup and slots [16*dch, 16*dch + 16), at tile rows [16w, 16w + 16).
-// Steps >= nd are sequence tiles of 64 keys starting at kt0.
+// Byte offset of 16-byte column chunk `ch` of tile row r.  A depth tile holds,
+// for every wave w, token w*tok_wave + dtok of the workgroup and slots
+// [16*dch, 16*dch + 16) at tile rows [16w, 16w + 16); a sequence tile holds
+// 64 keys starting at kt0.
 template <int D>
 __device__ __forceinline__ uint32_t tile_row_bytes(const Geo& g, bool depth, int kt0, int dtok, int dch, int r,
                                                    int ch) {
   if (!depth) return static_cast<uint32_t>(kt0 + r) * g.key_bytes + ch * 16;
   const int w = r / kDepthRowsPerWave;
   const int slot = dch * kDepthRowsPerWave + (r % kDepthRowsPerWave);
-  if (slot >= g.L) return kOutOfRange;
-  return static_cast<uint32_t>(w * g.tok_wave + dtok) * g.tok_bytes + static_cast<uint32_t>(slot) * (D * 2) +
-         ch * 16;
+  const uint32_t off = static_cast<uint32_t>(w * g.tok_wave + dtok) * g.tok_bytes +
+                       static_cast<uint32_t>(slot) * (D * 2) + ch * 16;
+  return slot < g.L ? off : kOutOfRange;  // a select, not a branch
 }
 
 // Register staging of one tile: each thread holds up to KCH 16-byte K chunks
@@ -116,20 +116,24 @@ struct Stage {
   u32x4 vr[VIT][4];
 };
 
+// Issue the global loads of depth tile `idx` (DEPTH_TILE) or sequence tile
+// `idx` into the thread's staging registers.
 template <int D, bool DEPTH_TILE>
-__device__ __forceinline__ void load_tile(Stage<D>& s, const Geo& g, int it, int nd, int nchunk, int tid) {
+__device__ __forceinline__ void load_tile(Stage<D>& s, const Geo& g, int idx, int nchunk, int tid) {
   constexpr int CH = Stage<D>::CH;
   constexpr bool depth = DEPTH_TILE;
-  const int dtok = depth ? it / nchunk : 0;
-  const int dch = depth ? it - dtok * nchunk : 0;
-  const int kt0 = depth ? 0 : (it - nd) * kBN;
+  const int dtok = depth ? idx / nchunk : 0;
+  const int dch = depth ? idx - dtok * nchunk : 0;
+  const int kt0 = depth ? 0 : idx * kBN;
   const __amdgpu_buffer_rsrc_t rk = depth ? g.kd : g.k;
   const __amdgpu_buffer_rsrc_t rv = depth ? g.vd : g.v;
+  constexpr bool k_full = Stage<D>::KCH * kThreads == kBN * CH;          // every thread has every K chunk
+  constexpr bool v_full = Stage<D>::VIT * kThreads == (kBN / 4) * CH;    // every thread has every V item
 #pragma unroll
   for (int x = 0; x < Stage<D>::KCH; ++x) {
     const int c = tid + x * kThreads;
-    uint32_t off = kOutOfRange;
-    if (c < kBN * CH) off = tile_row_bytes<D>(g, depth, kt0, dtok, dch, c / CH, c % CH);
+    uint32_t off = tile_row_bytes<D>(g, depth, kt0, dtok, dch, c / CH, c % CH);
+    if (!k_full) off = c < kBN * CH ? off : kOutOfRange;
     s.kc[x] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
   }
 #pragma unroll
@@ -138,8 +142,8 @@ __device__ __forceinline__ void load_tile(Stage<D>& s, const Geo& g, int it, int
     const int quad = item % (kBN / 4), oc = item / (kBN / 4);
 #pragma unroll
     for (int y = 0; y < 4; ++y) {
-      uint32_t off = kOutOfRange;
-      if (item < (kBN / 4) * CH) off = tile_row_bytes<D>(g, depth, kt0, dtok, dch, quad * 4 + y, oc);
+      uint32_t off = tile_row_bytes<D>(g, depth, kt0, dtok, dch, quad * 4 + y, oc);
+      if (!v_full) off = item < (kBN / 4) * CH ? off : kOutOfRange;
       s.vr[x][y] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
     }
   }
@@ -149,15 +153,17 @@ template <int D>
 __device__ __forceinline__ void store_tile(const Stage<D>& s, uint16_t* ks, uint16_t* vt, int tid) {
   constexpr int CH = Stage<D>::CH;
   constexpr int KS = Smem<D>::KS, VS = Smem<D>::VS;
+  constexpr bool k_full = Stage<D>::KCH * kThreads == kBN * CH;
+  constexpr bool v_full = Stage<D>::VIT * kThreads == (kBN / 4) * CH;
 #pragma unroll
   for (int x = 0; x < Stage<D>::KCH; ++x) {
     const int c = tid + x * kThreads;
-    if (c < kBN * CH) *reinterpret_cast<u32x4*>(ks + (c / CH) * KS + (c % CH) * 8) = s.kc[x];
+    if (k_full || c < kBN * CH) *reinterpret_cast<u32x4*>(ks + (c / CH) * KS + (c % CH) * 8) = s.kc[x];
   }
 #pragma unroll
   for (int x = 0; x < Stage<D>::VIT; ++x) {
     const int item = tid + x * kThreads;
-    if (item >= (kBN / 4) * CH) continue;
+    if (!v_full && item >= (kBN / 4) * CH) continue;
     const int quad = item % (kBN / 4), oc = item / (kBN / 4);
     const int pos = vpos(quad * 4);
     const u32x4* r = s.vr[x];
@@ -337,7 +343,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int ns = (kv_end + kBN - 1) / kBN;                         // sequence tiles
   const int nchunk = DEPTH ? (L + kDepthRowsPerWave - 1) / kDepthRowsPerWave : 1;  // 16-slot chunks per token
   const int nd = DEPTH ? g.tok_wave * nchunk : 0;                                  // depth tiles
-  const int ntot = nd + ns;
 
   // Q^T fragments (B operand): lane holds row my_row, d = 16*sl + 8*half + [0, 8).
   bf16x8 qf[D / 16];
@@ -362,26 +367,55 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // wave/2, score registers [8*(wave%2), 8*(wave%2) + 8).
   const int dj = wave >> 1, dh = wave & 1;
 
+  // ---- tile pipeline ------------------------------------------------------------
+  // Sequence tiles wholly before the workgroup's first token (and the sequence
+  // end) are unmasked for every wave; the few after them overlap the
+  // workgroup's own tokens and take the masked path.  The nd depth tiles are
+  // spread evenly among the unmasked ones -- depth tile d follows sequence
+  // tile (d+1)*n_int/nd - 1 -- so each depth load (a once-read HBM stream) is
+  // prefetched under a full sequence tile of MFMA work.  Every loop body is
+  // straight-line per wave, so the accumulator keeps its registers.
+  const int tb_first = row0 >> lgG;
+  const int n_int = CAUSAL ? min(ns, (tb_first + 1) / kBN) : T / kBN;
   Stage<D> stage;
-  if (nd > 0)
-    load_tile<D, true>(stage, g, 0, nd, nchunk, tid);
+  int pos = 0;  // pipeline position: selects the LDS buffer
+  int sq = 0;   // next sequence tile
+  if (DEPTH && nd > 0 && n_int / max(nd, 1) == 0)
+    load_tile<D, true>(stage, g, 0, nchunk, tid);
   else
-    load_tile<D, false>(stage, g, 0, nd, nchunk, tid);
+    load_tile<D, false>(stage, g, 0, nchunk, tid);
 
-  // ---- depth tiles: each wave sees only its own token's slots ----------------
   if constexpr (DEPTH) {
-    for (int it = 0; it < nd; ++it) {
-      uint16_t* ks = smem + (it & 1) * S::kBuf;
+    for (int d = 0; d < nd; ++d) {
+      const int s_end = ((d + 1) * n_int) / nd;
+      for (; sq < s_end; ++sq, ++pos) {
+        uint16_t* ks = smem + (pos & 1) * S::kBuf;
+        uint16_t* vt = ks + S::kK;
+        store_tile<D>(stage, ks, vt, tid);
+        __syncthreads();
+        if (sq + 1 < s_end)
+          load_tile<D, false>(stage, g, sq + 1, nchunk, tid);
+        else
+          load_tile<D, true>(stage, g, d, nchunk, tid);
+        seq_tile<D, false, CAUSAL>(st, qf, ks, vt, sq * kBN, T, my_t, r, half, scale_log2);
+      }
+      // depth tile d: each wave sees only its own token's slots
+      uint16_t* ks = smem + (pos & 1) * S::kBuf;
       uint16_t* vt = ks + S::kK;
       store_tile<D>(stage, ks, vt, tid);
       __syncthreads();
-      if (it + 1 < nd)
-        load_tile<D, true>(stage, g, it + 1, nd, nchunk, tid);
-      else if (ns > 0)
-        load_tile<D, false>(stage, g, it + 1, nd, nchunk, tid);
+      if (d + 1 < nd) {
+        if (sq < ((d + 2) * n_int) / nd)
+          load_tile<D, false>(stage, g, sq, nchunk, tid);
+        else
+          load_tile<D, true>(stage, g, d + 1, nchunk, tid);
+      } else if (sq < ns) {
+        load_tile<D, false>(stage, g, sq, nchunk, tid);
+      }
+      ++pos;
       const f32x16 sacc = qk_block<D>(qf, ks, 32 * dj, r, half);
-      const int dtok = it / nchunk;
-      const int slot0 = (it - dtok * nchunk) * kDepthRowsPerWave;
+      const int dtok = d / nchunk;
+      const int slot0 = (d - dtok * nchunk) * kDepthRowsPerWave;
       const bool mine = my_t == wt0 + dtok;
       float s[8];
 #pragma unroll
@@ -394,29 +428,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       pv_group<D>(st, pb[0], vt, 32 * dj + 16 * dh, r, half);
     }
   }
-
-  // ---- sequence tiles ----------------------------------------------------------
-  // Tiles wholly before the workgroup's first token and the sequence end are
-  // unmasked for every wave: one straight-line loop with no per-wave control
-  // flow (so the accumulator keeps its registers).  The remaining few tiles
-  // overlap the workgroup's own tokens and take the masked path.
-  const int tb_first = row0 >> lgG;
-  const int n_int = CAUSAL ? min(ns, (tb_first + 1) / kBN) : T / kBN;
-  for (int it = nd; it < nd + n_int; ++it) {
-    uint16_t* ks = smem + (it & 1) * S::kBuf;
+  for (; sq < n_int; ++sq, ++pos) {  // unmasked sequence tiles (all of them when there is no depth)
+    uint16_t* ks = smem + (pos & 1) * S::kBuf;
     uint16_t* vt = ks + S::kK;
     store_tile<D>(stage, ks, vt, tid);
     __syncthreads();
-    if (it + 1 < ntot) load_tile<D, false>(stage, g, it + 1, nd, nchunk, tid);
-    seq_tile<D, false, CAUSAL>(st, qf, ks, vt, (it - nd) * kBN, T, my_t, r, half, scale_log2);
+    if (sq + 1 < ns) load_tile<D, false>(stage, g, sq + 1, nchunk, tid);
+    seq_tile<D, false, CAUSAL>(st, qf, ks, vt, sq * kBN, T, my_t, r, half, scale_log2);
   }
-  for (int it = nd + n_int; it < ntot; ++it) {
-    uint16_t* ks = smem + (it & 1) * S::kBuf;
+  for (; sq < ns; ++sq, ++pos) {  // masked sequence tiles
+    uint16_t* ks = smem + (pos & 1) * S::kBuf;
     uint16_t* vt = ks + S::kK;
     store_tile<D>(stage, ks, vt, tid);
     __syncthreads();
-    if (it + 1 < ntot) load_tile<D, false>(stage, g, it + 1, nd, nchunk, tid);
-    const int kt0 = (it - nd) * kBN;
+    if (sq + 1 < ns) load_tile<D, false>(stage, g, sq + 1, nchunk, tid);
+    const int kt0 = sq * kBN;
     if (CAUSAL && kt0 > wt1) continue;  // nothing visible to this wave
     seq_tile<D, true, CAUSAL>(st, qf, ks, vt, kt0, T, my_t, r, half, scale_log2);
   }
