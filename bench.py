@@ -101,7 +101,27 @@ def _kernel_label(name):
     return None
 
 
-def summarize(trace_dir, fetch_dir, write_dir, command):
+def _sq_lines(sq_dir, command):
+    """Per-kernel SQ counter figures (one rocprofv3 --pmc pass)."""
+    vals = {}
+    for r in _read_csv(os.path.join(sq_dir, "run_counter_collection.csv")):
+        lab = _kernel_label(r["Kernel_Name"])
+        if lab:
+            vals.setdefault(lab, {})[r["Counter_Name"]] = float(r["Counter_Value"])
+    lines = ["", "SQ counters (one rocprofv3 --pmc pass):", "  command: " + command, ""]
+    for lab, v in sorted(vals.items()):
+        gui = v.get("GRBM_GUI_ACTIVE", 0.0)
+        simd_cycles = gui / 8.0 * 256 * 4  # GRBM_GUI_ACTIVE sums the 8 XCDs; 256 CUs x 4 SIMDs
+        lines.append("  %s: " % lab + ", ".join("%s=%.4g" % (k, x) for k, x in sorted(v.items())))
+        if gui and v.get("SQ_INSTS_MFMA"):
+            lines.append("    MFMA busy %.1f%% of SIMD cycles; VALU/MFMA instructions %.2f; LDS bank conflicts / "
+                         "LDS active %.4f" % (100.0 * v["SQ_VALU_MFMA_BUSY_CYCLES"] / simd_cycles,
+                                              v["SQ_INSTS_VALU"] / v["SQ_INSTS_MFMA"],
+                                              v["SQ_LDS_BANK_CONFLICT"] / max(1.0, v["SQ_LDS_IDX_ACTIVE"])))
+    return lines
+
+
+def summarize(trace_dir, fetch_dir, write_dir, command, sq_dir=None):
     """Turn rocprofv3 CSVs of this benchmark into the committed summary and traffic record.
 
     FETCH_SIZE / WRITE_SIZE are calibrated on the depth packer, a plain copy kernel of known
@@ -147,6 +167,8 @@ def summarize(trace_dir, fetch_dir, write_dir, command):
     alg = acc.algorithmic_bytes(shape)
     lines.append("  algorithmic bytes of the L=48 forward: %.4g B (traffic / algorithmic = %.3f)"
                  % (alg, traffic["moda_fwd_bf16 L=48"] / alg))
+    if sq_dir:
+        lines += _sq_lines(sq_dir, command[3] if len(command) > 3 else "")
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(os.path.join(os.path.dirname(TRAFFIC_FILE), "moda_fwd_bf16_long_L48.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -166,10 +188,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write the profiles/ summary from rocprofv3 CSV output directories and exit")
-    ap.add_argument("--commands", nargs=3, default=["", "", ""], help="the three rocprofv3 commands, for the record")
+    ap.add_argument("--sq", metavar="SQ_DIR", help="with --summarize: also summarise an SQ counter pass")
+    ap.add_argument("--commands", nargs="+", default=["", "", ""],
+                    help="the rocprofv3 commands (trace, fetch, write[, sq]), for the record")
     args = ap.parse_args()
     if args.summarize:
-        summarize(*args.summarize, command=args.commands)
+        summarize(*args.summarize, command=args.commands, sq_dir=args.sq)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: the MoDA forward has no multi-GPU path here (each (batch, KV head) "

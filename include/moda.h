@@ -71,7 +71,9 @@ typedef void* moda_stream_t; /* hipStream_t */
  * Errors: MODA_ERR_NULL (q, k_seq, v_seq, out or lse NULL; depth NULL with
  * L > 0); MODA_ERR_SHAPE (B, T, Hq, Hk or d <= 0, L < 0, Hq % Hk != 0,
  * causal not 0/1); MODA_ERR_UNSUPPORTED (d not 64 or 128; G not in
- * {1,2,4,8,16,32}); MODA_ERR_ALIGN; MODA_ERR_HIP.
+ * {1,2,4,8,16,32}; sizes beyond this build's limits: T*G, the workgroup count
+ * and, for this bf16 entry point, (T+64)*Hk*d*2 and 129*Hk*L*d*2 bytes must
+ * stay below 2^31); MODA_ERR_ALIGN; MODA_ERR_HIP.
  */
 int moda_attn_fwd(const void* q, const void* k_seq, const void* v_seq, const void* k_depth,
                   const void* v_depth, int B, int T, int Hq, int Hk, int d, int L, int causal,
@@ -80,7 +82,7 @@ int moda_attn_fwd(const void* q, const void* k_seq, const void* v_seq, const voi
 /*
  * The same operation with fp32 inputs and fp32 output, computed in fp32.
  * Arguments, layouts and errors are those of moda_attn_fwd with every bf16
- * tensor replaced by an fp32 one.
+ * tensor replaced by an fp32 one (without the bf16 byte-offset limits).
  */
 int moda_attn_fwd_f32(const void* q, const void* k_seq, const void* v_seq, const void* k_depth,
                       const void* v_depth, int B, int T, int Hq, int Hk, int d, int L, int causal,
