@@ -13,27 +13,32 @@
 //     (b, hk); each of its 4 waves owns 32 rows (32/G tokens).  The block's
 //     tokens are [t_start, t_end) with t_start = floor(row0/G) and
 //     t_end = floor(last/G) + 1; sequence keys at or past t_end are never read.
-//   * Every workgroup runs one pipeline of 64-row tiles staged in LDS, double
-//     buffered: while the waves compute on tile i, the global loads of tile
-//     i+1 are in flight in registers; one barrier per tile.  Two kinds:
+//   * Every workgroup runs one pipeline of 64-row K/V tiles in LDS, double
+//     buffered.  Tiles are staged by direct-to-LDS buffer loads (16 bytes per
+//     lane, no staging registers): the loads of tile i+1 are issued right
+//     after the barrier that publishes tile i, and each wave waits for its own
+//     loads before the next barrier.  Two kinds of tile:
 //       - sequence tiles of 64 keys, shared by all 4 waves;
 //       - depth tiles: 16 rows per wave, 16 consecutive slots of one of the
-//         wave's own tokens, read from the packed [B][T][Hk][L][d] stream
-//         (each (token, KV head) slab is one contiguous run, each depth
-//         element is read from HBM exactly once and used by the G rows of its
-//         token only), spread evenly among the sequence tiles.
+//         wave's own tokens, read from the packed [B][T][Hk][L][d] stream (each
+//         (token, KV head) slab is one contiguous run, each depth element is
+//         read from HBM exactly once and used by the G rows of its token
+//         only), spread evenly among the sequence tiles.
 //     Both kinds fold into the same running (max, sum, output) state of each
 //     row, so the softmax is one joint softmax over both candidate sets.
 //   * Scores are computed transposed, S^T = K * Q^T, on 32x32x16 bf16 MFMA with
 //     Q^T held in registers, so each lane owns one query row: the row max
 //     needs one cross-lane exchange (lane ^ 32) and the rescale of the output
 //     accumulator is per lane.  O^T += V^T * P^T takes the score registers,
-//     packed to bf16, directly as the B operand; V is written to LDS
-//     transposed (d-major) with the key order permuted to match the score
-//     register layout, so every MFMA operand is one 16-byte LDS read.
+//     packed to bf16, directly as the B operand; its A operand (V^T) is read
+//     from the row-major V tile with the transposing ds_read_b64_tr_b16, whose
+//     key order is chosen to match the score register layout.
+//   * LDS tiles are unpadded; 16-byte chunks are XOR-swizzled per row (K:
+//     chunk ^ row, V: chunk ^ 4*row, over the rows that share one LDS pass)
+//     so that the MFMA operand reads are bank-conflict free.
 //   * Softmax runs in base 2 with log2(e)/sqrt(d) folded into the exponent's
-//     FMA; the output rescale is skipped when no row max of the wave moved.
-//     lse is converted back to the natural log at the end.
+//     FMA; the output rescale is skipped unless a row max grows by more than
+//     2^8.  lse is converted back to the natural log at the end.
 //   * Causal workgroups are issued heaviest first (last row block first).
 #include "moda_device.h"
 #include "moda_launch.h"
@@ -48,24 +53,26 @@ constexpr int kBM = kWaves * kRowsPerWave;  // expanded rows per workgroup
 constexpr int kBN = 64;                     // rows (keys or depth slots) per tile
 constexpr int kDepthRowsPerWave = kBN / kWaves;
 
-template <int D>
-struct Smem {
-  static constexpr int KS = D + 8;    // K row stride (elements): +16 B breaks bank aliasing
-  static constexpr int VS = kBN + 8;  // V^T row stride
-  static constexpr int kK = kBN * KS;
-  static constexpr int kV = D * VS;
-  static constexpr int kBuf = kK + kV;
-  static constexpr int kElems = 2 * kBuf;
-};
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
-// Position of tile key `kk` inside a d-row of the transposed V tile.  Within
-// each 16-key group, key 8a + 4b + c is stored at 8b + 4a + c: the 8 keys that
-// lane half b holds in its score registers for one PV product become 8
-// consecutive elements (one 16-byte read).
-__device__ __forceinline__ int vpos(int kk) {
-  const int a = (kk >> 3) & 1, bb = (kk >> 2) & 1;
-  return (kk & ~15) | (bb << 3) | (a << 2) | (kk & 3);
-}
+// Tile geometry for head dimension D.  A tile row (one key or slot) is D*2
+// bytes = CH chunks of 16 bytes.  One DMA instruction of a wave fills 1 KiB =
+// RPI rows; each wave issues NX instructions per K (and per V) tile.
+template <int D>
+struct Tile {
+  static constexpr int ROW_BYTES = D * 2;
+  static constexpr int CH = D / 8;
+  static constexpr int RPI = 64 / CH;
+  static constexpr int NX = CH / kWaves;
+  static constexpr int BYTES = kBN * ROW_BYTES;  // one K or V tile
+  static constexpr int BUF = 2 * BYTES;          // K then V
+  static constexpr int RPB = 256 / ROW_BYTES;    // rows sharing one 256-byte bank row
+  // Chunk swizzles: logical chunk c of row r lives at physical chunk c ^ swz(r).
+  __device__ static __forceinline__ int swz_k(int row) { return (row / RPB) % CH; }
+  __device__ static __forceinline__ int swz_v(int row) { return 4 * ((row / RPB) % (CH / 4)); }
+};
 
 // Per-workgroup staging geometry.  All global tile reads are raw buffer loads
 // against four descriptors whose ranges end exactly at the last valid row, so
@@ -90,96 +97,40 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint16_t* base
                                            static_cast<int>(bytes), kBufFlags);
 }
 
-// Byte offset of 16-byte column chunk `ch` of tile row r.  A depth tile holds,
-// for every wave w, token w*tok_wave + dtok of the workgroup and slots
-// [16*dch, 16*dch + 16) at tile rows [16w, 16w + 16); a sequence tile holds
-// 64 keys starting at kt0.
-template <int D>
-__device__ __forceinline__ uint32_t tile_row_bytes(const Geo& g, bool depth, int kt0, int dtok, int dch, int r,
-                                                   int ch) {
-  if (!depth) return static_cast<uint32_t>(kt0 + r) * g.key_bytes + ch * 16;
-  const int w = r / kDepthRowsPerWave;
-  const int slot = dch * kDepthRowsPerWave + (r % kDepthRowsPerWave);
-  const uint32_t off = static_cast<uint32_t>(w * g.tok_wave + dtok) * g.tok_bytes +
-                       static_cast<uint32_t>(slot) * (D * 2) + ch * 16;
-  return slot < g.L ? off : kOutOfRange;  // a select, not a branch
-}
-
-// Register staging of one tile: each thread holds up to KCH 16-byte K chunks
-// and one (4-row, 8-column) V block per VIT item.
-template <int D>
-struct Stage {
-  static constexpr int CH = D / 8;                                  // 16-byte chunks per row
-  static constexpr int KCH = (kBN * CH + kThreads - 1) / kThreads;  // K chunks per thread
-  static constexpr int VIT = ((kBN / 4) * CH + kThreads - 1) / kThreads;
-  u32x4 kc[KCH];
-  u32x4 vr[VIT][4];
-};
-
-// Issue the global loads of depth tile `idx` (DEPTH_TILE) or sequence tile
-// `idx` into the thread's staging registers.
+// Issue the direct-to-LDS loads of one tile into `buf` (K at buf, V at
+// buf + BYTES).  Instruction x of wave w fills physical rows
+// pr = (w*NX + x)*RPI + lane/CH, physical chunk pc = lane % CH, with the
+// logical chunk pc ^ swz(pr) of global row pr.  A depth tile holds, for every
+// wave w, token w*tok_wave + dtok of the workgroup and slots
+// [16*dch, 16*dch + 16) at tile rows [16w, 16w + 16); a sequence tile holds 64
+// keys starting at kt0.
 template <int D, bool DEPTH_TILE>
-__device__ __forceinline__ void load_tile(Stage<D>& s, const Geo& g, int idx, int nchunk, int tid) {
-  constexpr int CH = Stage<D>::CH;
-  constexpr bool depth = DEPTH_TILE;
-  const int dtok = depth ? idx / nchunk : 0;
-  const int dch = depth ? idx - dtok * nchunk : 0;
-  const int kt0 = depth ? 0 : idx * kBN;
-  const __amdgpu_buffer_rsrc_t rk = depth ? g.kd : g.k;
-  const __amdgpu_buffer_rsrc_t rv = depth ? g.vd : g.v;
-  constexpr bool k_full = Stage<D>::KCH * kThreads == kBN * CH;          // every thread has every K chunk
-  constexpr bool v_full = Stage<D>::VIT * kThreads == (kBN / 4) * CH;    // every thread has every V item
+__device__ __forceinline__ void dma_tile(const Geo& g, int idx, int nchunk, uint8_t* buf, int wave, int lane) {
+  using TL = Tile<D>;
+  const int dtok = DEPTH_TILE ? idx / nchunk : 0;
+  const int dch = DEPTH_TILE ? idx - dtok * nchunk : 0;
+  const int kt0 = DEPTH_TILE ? 0 : idx * kBN;
+  const __amdgpu_buffer_rsrc_t rk = DEPTH_TILE ? g.kd : g.k;
+  const __amdgpu_buffer_rsrc_t rv = DEPTH_TILE ? g.vd : g.v;
 #pragma unroll
-  for (int x = 0; x < Stage<D>::KCH; ++x) {
-    const int c = tid + x * kThreads;
-    uint32_t off = tile_row_bytes<D>(g, depth, kt0, dtok, dch, c / CH, c % CH);
-    if (!k_full) off = c < kBN * CH ? off : kOutOfRange;
-    s.kc[x] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
-  }
-#pragma unroll
-  for (int x = 0; x < Stage<D>::VIT; ++x) {
-    const int item = tid + x * kThreads;
-    const int quad = item % (kBN / 4), oc = item / (kBN / 4);
-#pragma unroll
-    for (int y = 0; y < 4; ++y) {
-      uint32_t off = tile_row_bytes<D>(g, depth, kt0, dtok, dch, quad * 4 + y, oc);
-      if (!v_full) off = item < (kBN / 4) * CH ? off : kOutOfRange;
-      s.vr[x][y] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+  for (int x = 0; x < TL::NX; ++x) {
+    const int pr = (wave * TL::NX + x) * TL::RPI + lane / TL::CH;
+    const int pc = lane % TL::CH;
+    uint32_t row_off;
+    bool valid = true;
+    if (DEPTH_TILE) {
+      const int slot = dch * kDepthRowsPerWave + (pr % kDepthRowsPerWave);
+      row_off = static_cast<uint32_t>(wave * g.tok_wave + dtok) * g.tok_bytes +
+                static_cast<uint32_t>(slot) * TL::ROW_BYTES;
+      valid = slot < g.L;
+    } else {
+      row_off = static_cast<uint32_t>(kt0 + pr) * g.key_bytes;
     }
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void store_tile(const Stage<D>& s, uint16_t* ks, uint16_t* vt, int tid) {
-  constexpr int CH = Stage<D>::CH;
-  constexpr int KS = Smem<D>::KS, VS = Smem<D>::VS;
-  constexpr bool k_full = Stage<D>::KCH * kThreads == kBN * CH;
-  constexpr bool v_full = Stage<D>::VIT * kThreads == (kBN / 4) * CH;
-#pragma unroll
-  for (int x = 0; x < Stage<D>::KCH; ++x) {
-    const int c = tid + x * kThreads;
-    if (k_full || c < kBN * CH) *reinterpret_cast<u32x4*>(ks + (c / CH) * KS + (c % CH) * 8) = s.kc[x];
-  }
-#pragma unroll
-  for (int x = 0; x < Stage<D>::VIT; ++x) {
-    const int item = tid + x * kThreads;
-    if (!v_full && item >= (kBN / 4) * CH) continue;
-    const int quad = item % (kBN / 4), oc = item / (kBN / 4);
-    const int pos = vpos(quad * 4);
-    const u32x4* r = s.vr[x];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int w = e >> 1;
-      uint32_t lo, hi;
-      if (e & 1) {
-        lo = (r[0][w] >> 16) | (r[1][w] & 0xffff0000u);
-        hi = (r[2][w] >> 16) | (r[3][w] & 0xffff0000u);
-      } else {
-        lo = (r[0][w] & 0xffffu) | (r[1][w] << 16);
-        hi = (r[2][w] & 0xffffu) | (r[3][w] << 16);
-      }
-      *reinterpret_cast<u32x2*>(vt + (oc * 8 + e) * VS + pos) = u32x2{lo, hi};
-    }
+    const uint32_t ok = valid ? row_off + ((pc ^ TL::swz_k(pr)) * 16) : kOutOfRange;  // selects, not branches
+    const uint32_t ov = valid ? row_off + ((pc ^ TL::swz_v(pr)) * 16) : kOutOfRange;
+    uint8_t* dk = buf + (wave * TL::NX + x) * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)dk, 16, ok, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(dk + TL::BYTES), 16, ov, 0, 0, 0);
   }
 }
 
@@ -233,28 +184,45 @@ __device__ __forceinline__ void online_update(RowState<D>& st, float (&s)[N], bf
   }
 }
 
-// S^T block: 32 keys (rows of ks starting at key0) x the wave's 32 query rows.
+// S^T block: 32 keys (K tile rows key0 .. key0+31) x the wave's 32 query rows.
+// Lane l supplies key row key0 + l%32, logical chunk 2*sl + l/32 of each slice.
 template <int D>
-__device__ __forceinline__ f32x16 qk_block(const bf16x8 (&qf)[D / 16], const uint16_t* ks, int key0, int r,
+__device__ __forceinline__ f32x16 qk_block(const bf16x8 (&qf)[D / 16], const uint8_t* kt, int key0, int r,
                                            int half) {
-  constexpr int KS = Smem<D>::KS;
+  using TL = Tile<D>;
+  const int row = key0 + r;
+  const uint8_t* rowp = kt + row * TL::ROW_BYTES;
+  const int sw = TL::swz_k(row);
   f32x16 s = {};
 #pragma unroll
   for (int sl = 0; sl < D / 16; ++sl) {
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + (key0 + r) * KS + sl * 16 + half * 8);
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(rowp + (((2 * sl + half) ^ sw) * 16));
     s = mfma32(a, qf[sl], s);
   }
   return s;
 }
 
-// O^T += V^T * P^T for one 16-key group starting at tile key key0 + 16*h.
+// O^T += V^T * P^T for the 16-key group starting at tile key key16 (a multiple
+// of 16).  The B operand pb holds, in lane half hf, the weights of keys
+// key16 + 4*hf + {0..3} and key16 + 8 + 4*hf + {0..3}.  The A operand is read
+// with two transposing LDS reads: lane i of each 16-lane group points at row
+// key_b + i/4, columns d0 + 4*(i%4) .. +3, and receives V[key_b + k][d0 + i]
+// for k = 0..3.
 template <int D>
-__device__ __forceinline__ void pv_group(RowState<D>& st, const bf16x8& pb, const uint16_t* vt, int key16, int r,
-                                         int half) {
-  constexpr int VS = Smem<D>::VS;
+__device__ __forceinline__ void pv_group(RowState<D>& st, const bf16x8& pb, const uint8_t* vtile, int key16,
+                                         int lane) {
+  using TL = Tile<D>;
+  const int i = lane & 15, q = (lane >> 4) & 1, hf = lane >> 5;
+  const int row0 = key16 + 4 * hf + (i >> 2);  // first read; the second is 8 rows further
+  const int sw0 = TL::swz_v(row0), sw1 = TL::swz_v(row0 + 8);
+  const uint8_t* p0 = vtile + row0 * TL::ROW_BYTES + 8 * (i & 1);
+  const uint8_t* p1 = p0 + 8 * TL::ROW_BYTES;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(vt + (dt * 32 + r) * VS + key16 + 8 * half);
+    const int lc = (32 * dt + 16 * q) / 8 + ((i & 3) >> 1);  // logical 16-byte chunk of column d0 + 4*(i%4)
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p0 + ((lc ^ sw0) * 16)));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p1 + ((lc ^ sw1) * 16)));
+    const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     st.o[dt] = mfma32(a, pb, st.o[dt]);
   }
 }
@@ -263,12 +231,12 @@ __device__ __forceinline__ void pv_group(RowState<D>& st, const bf16x8& pb, cons
 // state and multiplied into O^T.  MASK applies the causal / sequence-end mask
 // (branch-free selects); interior tiles take the MASK = false path.
 template <int D, bool MASK, bool CAUSAL>
-__device__ __forceinline__ void seq_tile(RowState<D>& st, const bf16x8 (&qf)[D / 16], const uint16_t* ks,
-                                         const uint16_t* vt, int kt0, int T, int my_t, int r, int half,
-                                         float scale) {
+__device__ __forceinline__ void seq_tile(RowState<D>& st, const bf16x8 (&qf)[D / 16], const uint8_t* buf,
+                                         int kt0, int T, int my_t, int lane, float scale) {
+  const int r = lane & 31, half = lane >> 5;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const f32x16 sacc = qk_block<D>(qf, ks, 32 * j, r, half);
+    const f32x16 sacc = qk_block<D>(qf, buf, 32 * j, r, half);
     float s[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -282,8 +250,14 @@ __device__ __forceinline__ void seq_tile(RowState<D>& st, const bf16x8 (&qf)[D /
     bf16x8 pb[2];
     online_update<D, 16>(st, s, pb, scale);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) pv_group<D>(st, pb[h], vt, 32 * j + 16 * h, r, half);
+    for (int h = 0; h < 2; ++h) pv_group<D>(st, pb[h], buf + Tile<D>::BYTES, 32 * j + 16 * h, lane);
   }
+}
+
+// Publish the tile this wave's DMA loads filled: wait for them, then barrier.
+__device__ __forceinline__ void publish_tile() {
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+  __syncthreads();
 }
 
 template <int D, bool DEPTH, bool CAUSAL>
@@ -291,8 +265,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ kd, const uint16_t* __restrict__ vd, int B, int T, int Hq, int Hk, int L,
     int lgG, int nrb, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
-  using S = Smem<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[S::kElems];
+  using TL = Tile<D>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * TL::BUF];
 
   const int G = 1 << lgG;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -302,7 +276,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int bid = blockIdx.x;
   const int rb = CAUSAL ? (nrb - 1 - bid / nbh) : (bid / nbh);
   const int bh = bid % nbh;
-
   const int b = bh / Hk, hk = bh % Hk;
   const int row0 = rb * kBM;
   const int TG = T << lgG;
@@ -362,8 +335,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   st.m = -INFINITY;
   st.l = 0.0f;
 
-  // In depth tile it this wave's 16 rows (token wt0 + it / nchunk, slots from
-  // 16 * (it % nchunk)) sit at tile rows [16*wave, 16*wave + 16): 32-key block
+  // In depth tile d this wave's 16 rows (token wt0 + d / nchunk, slots from
+  // 16 * (d % nchunk)) sit at tile rows [16*wave, 16*wave + 16): 32-key block
   // wave/2, score registers [8*(wave%2), 8*(wave%2) + 8).
   const int dj = wave >> 1, dh = wave & 1;
 
@@ -375,45 +348,41 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // tile (d+1)*n_int/nd - 1 -- so each depth load (a once-read HBM stream) is
   // prefetched under a full sequence tile of MFMA work.  Every loop body is
   // straight-line per wave, so the accumulator keeps its registers.
-  const int tb_first = row0 >> lgG;
-  const int n_int = CAUSAL ? min(ns, (tb_first + 1) / kBN) : T / kBN;
-  Stage<D> stage;
+  const int n_int = CAUSAL ? min(ns, (tb + 1) / kBN) : T / kBN;
   int pos = 0;  // pipeline position: selects the LDS buffer
   int sq = 0;   // next sequence tile
   if (DEPTH && nd > 0 && n_int / max(nd, 1) == 0)
-    load_tile<D, true>(stage, g, 0, nchunk, tid);
+    dma_tile<D, true>(g, 0, nchunk, smem, wave, lane);
   else
-    load_tile<D, false>(stage, g, 0, nchunk, tid);
+    dma_tile<D, false>(g, 0, nchunk, smem, wave, lane);
 
   if constexpr (DEPTH) {
     for (int d = 0; d < nd; ++d) {
       const int s_end = ((d + 1) * n_int) / nd;
       for (; sq < s_end; ++sq, ++pos) {
-        uint16_t* ks = smem + (pos & 1) * S::kBuf;
-        uint16_t* vt = ks + S::kK;
-        store_tile<D>(stage, ks, vt, tid);
-        __syncthreads();
+        uint8_t* cur = smem + (pos & 1) * TL::BUF;
+        uint8_t* nxt = smem + ((pos + 1) & 1) * TL::BUF;
+        publish_tile();
         if (sq + 1 < s_end)
-          load_tile<D, false>(stage, g, sq + 1, nchunk, tid);
+          dma_tile<D, false>(g, sq + 1, nchunk, nxt, wave, lane);
         else
-          load_tile<D, true>(stage, g, d, nchunk, tid);
-        seq_tile<D, false, CAUSAL>(st, qf, ks, vt, sq * kBN, T, my_t, r, half, scale_log2);
+          dma_tile<D, true>(g, d, nchunk, nxt, wave, lane);
+        seq_tile<D, false, CAUSAL>(st, qf, cur, sq * kBN, T, my_t, lane, scale_log2);
       }
       // depth tile d: each wave sees only its own token's slots
-      uint16_t* ks = smem + (pos & 1) * S::kBuf;
-      uint16_t* vt = ks + S::kK;
-      store_tile<D>(stage, ks, vt, tid);
-      __syncthreads();
+      uint8_t* cur = smem + (pos & 1) * TL::BUF;
+      uint8_t* nxt = smem + ((pos + 1) & 1) * TL::BUF;
+      publish_tile();
       if (d + 1 < nd) {
         if (sq < ((d + 2) * n_int) / nd)
-          load_tile<D, false>(stage, g, sq, nchunk, tid);
+          dma_tile<D, false>(g, sq, nchunk, nxt, wave, lane);
         else
-          load_tile<D, true>(stage, g, d + 1, nchunk, tid);
+          dma_tile<D, true>(g, d + 1, nchunk, nxt, wave, lane);
       } else if (sq < ns) {
-        load_tile<D, false>(stage, g, sq, nchunk, tid);
+        dma_tile<D, false>(g, sq, nchunk, nxt, wave, lane);
       }
       ++pos;
-      const f32x16 sacc = qk_block<D>(qf, ks, 32 * dj, r, half);
+      const f32x16 sacc = qk_block<D>(qf, cur, 32 * dj, r, half);
       const int dtok = d / nchunk;
       const int slot0 = (d - dtok * nchunk) * kDepthRowsPerWave;
       const bool mine = my_t == wt0 + dtok;
@@ -425,26 +394,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       }
       bf16x8 pb[1];
       online_update<D, 8>(st, s, pb, scale_log2);
-      pv_group<D>(st, pb[0], vt, 32 * dj + 16 * dh, r, half);
+      pv_group<D>(st, pb[0], cur + TL::BYTES, 32 * dj + 16 * dh, lane);
     }
   }
   for (; sq < n_int; ++sq, ++pos) {  // unmasked sequence tiles (all of them when there is no depth)
-    uint16_t* ks = smem + (pos & 1) * S::kBuf;
-    uint16_t* vt = ks + S::kK;
-    store_tile<D>(stage, ks, vt, tid);
-    __syncthreads();
-    if (sq + 1 < ns) load_tile<D, false>(stage, g, sq + 1, nchunk, tid);
-    seq_tile<D, false, CAUSAL>(st, qf, ks, vt, sq * kBN, T, my_t, r, half, scale_log2);
+    uint8_t* cur = smem + (pos & 1) * TL::BUF;
+    uint8_t* nxt = smem + ((pos + 1) & 1) * TL::BUF;
+    publish_tile();
+    if (sq + 1 < ns) dma_tile<D, false>(g, sq + 1, nchunk, nxt, wave, lane);
+    seq_tile<D, false, CAUSAL>(st, qf, cur, sq * kBN, T, my_t, lane, scale_log2);
   }
   for (; sq < ns; ++sq, ++pos) {  // masked sequence tiles
-    uint16_t* ks = smem + (pos & 1) * S::kBuf;
-    uint16_t* vt = ks + S::kK;
-    store_tile<D>(stage, ks, vt, tid);
-    __syncthreads();
-    if (sq + 1 < ns) load_tile<D, false>(stage, g, sq + 1, nchunk, tid);
+    uint8_t* cur = smem + (pos & 1) * TL::BUF;
+    uint8_t* nxt = smem + ((pos + 1) & 1) * TL::BUF;
+    publish_tile();
+    if (sq + 1 < ns) dma_tile<D, false>(g, sq + 1, nchunk, nxt, wave, lane);
     const int kt0 = sq * kBN;
     if (CAUSAL && kt0 > wt1) continue;  // nothing visible to this wave
-    seq_tile<D, true, CAUSAL>(st, qf, ks, vt, kt0, T, my_t, r, half, scale_log2);
+    seq_tile<D, true, CAUSAL>(st, qf, cur, kt0, T, my_t, lane, scale_log2);
   }
 
   // ---- epilogue --------------------------------------------------------------
