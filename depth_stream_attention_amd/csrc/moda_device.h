@@ -40,6 +40,17 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ void swap_halves(float& a, float& b) {
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
 }
+// Returns x through an empty asm statement, hiding its value from the
+// optimiser at this point: values derived from it are then computed here
+// instead of being hoisted out of a loop and held in registers across it.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+__device__ __forceinline__ int opaque_s(int x) {  // the same for a wave-uniform value
+  asm volatile("" : "+s"(x));
+  return x;
+}
 __device__ __forceinline__ float pair_max(float x) {
   float a = x, b = x;
   swap_halves(a, b);

@@ -53,9 +53,23 @@ constexpr int kBM = kWaves * kRowsPerWave;  // expanded rows per workgroup
 constexpr int kBN = 64;                     // rows (keys or depth slots) per tile
 constexpr int kDepthRowsPerWave = kBN / kWaves;
 
+// LDS pointers are kept in address space 3 (32-bit) so tile addressing is
+// plain 32-bit arithmetic.
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8_t;
+
+// The LDS object at byte address addr.  (Built from the integer: the null
+// pointer of the LDS address space is not address 0.)
+template <typename T>
+__device__ __forceinline__ T* lds_at(uint32_t addr) {
+  return reinterpret_cast<T*>(static_cast<uintptr_t>(addr));
+}
+__device__ __forceinline__ uint32_t lds_addr(const lds_u8* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
 
 // Tile geometry for head dimension D.  A tile row (one key or slot) is D*2
 // bytes = CH chunks of 16 bytes.  One DMA instruction of a wave fills 1 KiB =
@@ -82,7 +96,7 @@ struct Tile {
 //   depth   : base &x[b][t_b][hk][0][0] with t_b the workgroup's first token;
 //             token t_b + u, slot i at byte (u*Hk*L + i) * d*2.
 struct Geo {
-  __amdgpu_buffer_rsrc_t k, v, kd, vd;
+  __amdgpu_buffer_rsrc_t kd, vd;
   int L;
   uint32_t key_bytes;   // Hk*d*2: stride between consecutive keys of one KV head
   uint32_t tok_bytes;   // Hk*L*d*2: stride between consecutive tokens' depth slabs
@@ -97,40 +111,31 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint16_t* base
                                            static_cast<int>(bytes), kBufFlags);
 }
 
-// Issue the direct-to-LDS loads of one tile into `buf` (K at buf, V at
-// buf + BYTES).  Instruction x of wave w fills physical rows
-// pr = (w*NX + x)*RPI + lane/CH, physical chunk pc = lane % CH, with the
-// logical chunk pc ^ swz(pr) of global row pr.  A depth tile holds, for every
-// wave w, token w*tok_wave + dtok of the workgroup and slots
-// [16*dch, 16*dch + 16) at tile rows [16w, 16w + 16); a sequence tile holds 64
-// keys starting at kt0.
-template <int D, bool DEPTH_TILE>
-__device__ __forceinline__ void dma_tile(const Geo& g, int idx, int nchunk, uint8_t* buf, int wave, int lane) {
+// Direct-to-LDS loads of depth tile `idx` into `buf` (K at buf, V at
+// buf + BYTES).  For every wave w the tile holds token w*tok_wave + dtok of
+// the workgroup, slots [16*dch, 16*dch + 16), at tile rows [16w, 16w + 16).
+// Instruction x of wave w fills tile rows pr = (w*NX + x)*RPI + lane/CH,
+// physical chunk pc = lane % CH, with logical chunk pc ^ swz(pr).  Padding
+// slots (>= L) get an offset past the descriptor range and read as zero.
+template <int D>
+__device__ __forceinline__ void dma_depth(const Geo& g, int idx, int nchunk, lds_u8* buf, int wave, int lane) {
   using TL = Tile<D>;
-  const int dtok = DEPTH_TILE ? idx / nchunk : 0;
-  const int dch = DEPTH_TILE ? idx - dtok * nchunk : 0;
-  const int kt0 = DEPTH_TILE ? 0 : idx * kBN;
-  const __amdgpu_buffer_rsrc_t rk = DEPTH_TILE ? g.kd : g.k;
-  const __amdgpu_buffer_rsrc_t rv = DEPTH_TILE ? g.vd : g.v;
+  lane = opaque(lane);  // per-lane offsets below are recomputed per tile, not held across the loop
+  const int dtok = idx / nchunk;
+  const int dch = idx - dtok * nchunk;
 #pragma unroll
   for (int x = 0; x < TL::NX; ++x) {
     const int pr = (wave * TL::NX + x) * TL::RPI + lane / TL::CH;
     const int pc = lane % TL::CH;
-    uint32_t row_off;
-    bool valid = true;
-    if (DEPTH_TILE) {
-      const int slot = dch * kDepthRowsPerWave + (pr % kDepthRowsPerWave);
-      row_off = static_cast<uint32_t>(wave * g.tok_wave + dtok) * g.tok_bytes +
-                static_cast<uint32_t>(slot) * TL::ROW_BYTES;
-      valid = slot < g.L;
-    } else {
-      row_off = static_cast<uint32_t>(kt0 + pr) * g.key_bytes;
-    }
+    const int slot = dch * kDepthRowsPerWave + (pr % kDepthRowsPerWave);
+    const uint32_t row_off = static_cast<uint32_t>(wave * g.tok_wave + dtok) * g.tok_bytes +
+                             static_cast<uint32_t>(slot) * TL::ROW_BYTES;
+    const bool valid = slot < g.L;
     const uint32_t ok = valid ? row_off + ((pc ^ TL::swz_k(pr)) * 16) : kOutOfRange;  // selects, not branches
     const uint32_t ov = valid ? row_off + ((pc ^ TL::swz_v(pr)) * 16) : kOutOfRange;
-    uint8_t* dk = buf + (wave * TL::NX + x) * 1024;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)dk, 16, ok, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(dk + TL::BYTES), 16, ov, 0, 0, 0);
+    lds_u8* dk = buf + (wave * TL::NX + x) * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(g.kd, (lds_void_t*)dk, 16, ok, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(g.vd, (lds_void_t*)(dk + TL::BYTES), 16, ov, 0, 0, 0);
   }
 }
 
@@ -148,6 +153,25 @@ struct RowState {
 // quotient; the final division and lse use the offset actually applied.
 constexpr float kRescaleSlack = 8.0f;
 
+// acc *= alpha, element by element in the accumulator's own registers.  As
+// plain code the multiply gets fresh destination registers and, once the
+// conditional rescale merges back, every tile pays a copy of the whole
+// accumulator; tying each element's input and output keeps it in place.
+// alpha comes straight from v_exp: the first multiply after it waits out the
+// transcendental-result hazard (inline asm is invisible to the compiler's
+// hazard checks).
+__device__ __forceinline__ void scale_in_place(f32x16& acc, float alpha, bool first) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float x = acc[i];
+    if (first && i == 0)
+      asm volatile("s_nop 1\n\tv_mul_f32 %0, %0, %1" : "+v"(x) : "v"(alpha));
+    else
+      asm volatile("v_mul_f32 %0, %0, %1" : "+v"(x) : "v"(alpha));
+    acc[i] = x;
+  }
+}
+
 // Fold N raw scores (-inf = masked) into the state and return the weights,
 // packed to bf16 in groups of 8 (one PV B operand per group).
 template <int D, int N>
@@ -162,9 +186,7 @@ __device__ __forceinline__ void online_update(RowState<D>& st, float (&s)[N], bf
     const float alpha = fast_exp2(st.m - (m_new == -INFINITY ? 0.0f : m_new));
     st.l *= alpha;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) st.o[dt][i] *= alpha;
+    for (int dt = 0; dt < D / 32; ++dt) scale_in_place(st.o[dt], alpha, dt == 0);
     st.m = m_new;
   }
   const float base = (st.m == -INFINITY) ? 0.0f : st.m;
@@ -184,59 +206,128 @@ __device__ __forceinline__ void online_update(RowState<D>& st, float (&s)[N], bf
   }
 }
 
-// S^T block: 32 keys (K tile rows key0 .. key0+31) x the wave's 32 query rows.
-// Lane l supplies key row key0 + l%32, logical chunk 2*sl + l/32 of each slice.
+// Per-lane LDS and DMA offsets, computed once.  In the tile loop every LDS
+// read address is (buffer base + one of these) plus a compile-time immediate
+// (the 32-key block, 16-key group or second half of a transposed read), so a
+// tile costs one add per distinct register instead of a full address
+// computation per read, and the sequence-tile loads need no address work.
 template <int D>
-__device__ __forceinline__ f32x16 qk_block(const bf16x8 (&qf)[D / 16], const uint8_t* kt, int key0, int r,
-                                           int half) {
+struct LaneOffs {
+  uint32_t kr[D / 16];                        // K read of slice sl, tile rows 0..31 (rows 32..63: + 32 rows)
+  uint32_t vr[D / 32];                        // V transposed read of d tile dt, keys 0..15 (others: + rows)
+  uint32_t dk[Tile<D>::NX], dv[Tile<D>::NX];  // sequence-tile loads, relative to the tile's first key
+};
+
+template <int D>
+__device__ __forceinline__ void init_offsets(LaneOffs<D>& lo, int lane, int wave, uint32_t key_bytes) {
   using TL = Tile<D>;
-  const int row = key0 + r;
-  const uint8_t* rowp = kt + row * TL::ROW_BYTES;
-  const int sw = TL::swz_k(row);
+  const int r = lane & 31, half = lane >> 5;
+#pragma unroll
+  for (int sl = 0; sl < D / 16; ++sl) lo.kr[sl] = r * TL::ROW_BYTES + (((2 * sl + half) ^ TL::swz_k(r)) * 16);
+  const int i = lane & 15, q = (lane >> 4) & 1, hf = lane >> 5;
+  const int row0 = 4 * hf + (i >> 2);  // the second read is 8 rows further (same swizzle)
+  const int sw = TL::swz_v(row0);
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    const int lc = (32 * dt + 16 * q) / 8 + ((i & 3) >> 1);  // logical chunk of column d0 + 4*(i%4)
+    lo.vr[dt] = row0 * TL::ROW_BYTES + 8 * (i & 1) + ((lc ^ sw) * 16);
+  }
+  // Load instruction x of wave w fills tile rows pr = (w*NX + x)*RPI + lane/CH,
+  // physical chunk pc = lane % CH, with logical chunk pc ^ swz(pr).
+#pragma unroll
+  for (int x = 0; x < TL::NX; ++x) {
+    const int pr = (wave * TL::NX + x) * TL::RPI + lane / TL::CH;
+    const int pc = lane % TL::CH;
+    lo.dk[x] = static_cast<uint32_t>(pr) * key_bytes + ((pc ^ TL::swz_k(pr)) * 16);
+    lo.dv[x] = static_cast<uint32_t>(pr) * key_bytes + ((pc ^ TL::swz_v(pr)) * 16);
+  }
+}
+
+// Direct-to-LDS loads of sequence tile `idx` into `buf` (K at buf, V at
+// buf + BYTES), through descriptors rebased to the tile's first key (scalar
+// work), so the per-lane offsets are loop invariant.  Keys past the sequence
+// end fall outside the range and read as zero.
+template <int D>
+__device__ __forceinline__ void dma_seq(const uint16_t* kb, const uint16_t* vb, uint32_t seq_range,
+                                        uint32_t key_bytes, int Hk, int idx, lds_u8* buf, int wave,
+                                        const LaneOffs<D>& lo) {
+  using TL = Tile<D>;
+  const int64_t first = static_cast<int64_t>(idx) * kBN * Hk * D;  // elements
+  const uint32_t range = seq_range - static_cast<uint32_t>(idx * kBN) * key_bytes;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb + first, range);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb + first, range);
+#pragma unroll
+  for (int x = 0; x < TL::NX; ++x) {
+    lds_u8* dk = buf + (wave * TL::NX + x) * 1024;
+    const uint32_t ok = lo.dk[x], ov = lo.dv[x];
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)dk, 16, ok, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(dk + TL::BYTES), 16, ov, 0, 0, 0);
+  }
+}
+
+// S^T block: 32 keys x the wave's 32 query rows.  kt[sl] holds the lane's
+// read address of slice sl for the block's first row; lane l supplies key row
+// l%32, logical chunk 2*sl + l/32.
+template <int D>
+__device__ __forceinline__ f32x16 qk_block(const bf16x8 (&qf)[D / 16], const uint32_t (&kt)[D / 16], int row_bytes_off) {
   f32x16 s = {};
 #pragma unroll
   for (int sl = 0; sl < D / 16; ++sl) {
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(rowp + (((2 * sl + half) ^ sw) * 16));
+    const bf16x8 a = *lds_at<lds_bf16x8_t>(kt[sl] + row_bytes_off);
     s = mfma32(a, qf[sl], s);
   }
   return s;
 }
 
-// O^T += V^T * P^T for the 16-key group starting at tile key key16 (a multiple
-// of 16).  The B operand pb holds, in lane half hf, the weights of keys
-// key16 + 4*hf + {0..3} and key16 + 8 + 4*hf + {0..3}.  The A operand is read
-// with two transposing LDS reads: lane i of each 16-lane group points at row
-// key_b + i/4, columns d0 + 4*(i%4) .. +3, and receives V[key_b + k][d0 + i]
+// O^T += V^T * P^T for one 16-key group whose first V row is `off` bytes past
+// the addresses in vt.  The B operand pb holds, in lane half hf, the weights
+// of keys 4*hf + {0..3} and 8 + 4*hf + {0..3} of the group.  The A operand is
+// read with two transposing LDS reads: lane i of each 16-lane group points at
+// row key_b + i/4, columns d0 + 4*(i%4) .. +3, and receives V[key_b + k][d0 + i]
 // for k = 0..3.
 template <int D>
-__device__ __forceinline__ void pv_group(RowState<D>& st, const bf16x8& pb, const uint8_t* vtile, int key16,
-                                         int lane) {
+__device__ __forceinline__ void pv_group(RowState<D>& st, const bf16x8& pb, const uint32_t (&vt)[D / 32], int off) {
   using TL = Tile<D>;
-  const int i = lane & 15, q = (lane >> 4) & 1, hf = lane >> 5;
-  const int row0 = key16 + 4 * hf + (i >> 2);  // first read; the second is 8 rows further
-  const int sw0 = TL::swz_v(row0), sw1 = TL::swz_v(row0 + 8);
-  const uint8_t* p0 = vtile + row0 * TL::ROW_BYTES + 8 * (i & 1);
-  const uint8_t* p1 = p0 + 8 * TL::ROW_BYTES;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
-    const int lc = (32 * dt + 16 * q) / 8 + ((i & 3) >> 1);  // logical 16-byte chunk of column d0 + 4*(i%4)
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p0 + ((lc ^ sw0) * 16)));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p1 + ((lc ^ sw1) * 16)));
-    const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_at<lds_s16x4_t>(vt[dt] + off));
+    const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_at<lds_s16x4_t>(vt[dt] + off + 8 * TL::ROW_BYTES));
+    const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
     st.o[dt] = mfma32(a, pb, st.o[dt]);
   }
 }
 
+// Absolute LDS addresses of this tile's K and V reads: one add per register.
+template <int D>
+struct TileAddr {
+  uint32_t k[D / 16];
+  uint32_t v[D / 32];
+};
+
+template <int D>
+__device__ __forceinline__ TileAddr<D> tile_addr(const lds_u8* buf, const LaneOffs<D>& lo) {
+  TileAddr<D> a;
+  const uint32_t base = lds_addr(buf);
+#pragma unroll
+  for (int sl = 0; sl < D / 16; ++sl) a.k[sl] = base + lo.kr[sl];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) a.v[dt] = base + Tile<D>::BYTES + lo.vr[dt];
+  return a;
+}
+
 // One 64-key sequence tile: two 32-key blocks of S^T, each folded into the
 // state and multiplied into O^T.  MASK applies the causal / sequence-end mask
-// (branch-free selects); interior tiles take the MASK = false path.
+// (branch-free selects); interior tiles take MASK = false.
 template <int D, bool MASK, bool CAUSAL>
-__device__ __forceinline__ void seq_tile(RowState<D>& st, const bf16x8 (&qf)[D / 16], const uint8_t* buf,
-                                         int kt0, int T, int my_t, int lane, float scale) {
-  const int r = lane & 31, half = lane >> 5;
+__device__ __forceinline__ void seq_tile(RowState<D>& st, const bf16x8 (&qf)[D / 16], const TileAddr<D>& ta,
+                                         int kt0, int T, int my_t, int half, float scale) {
+  using TL = Tile<D>;
+  f32x16 sq[2];
+  sq[0] = qk_block<D>(qf, ta.k, 0);
+  sq[1] = qk_block<D>(qf, ta.k, 32 * TL::ROW_BYTES);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const f32x16 sacc = qk_block<D>(qf, buf, 32 * j, r, half);
+    const f32x16 sacc = sq[j];
     float s[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -250,7 +341,7 @@ __device__ __forceinline__ void seq_tile(RowState<D>& st, const bf16x8 (&qf)[D /
     bf16x8 pb[2];
     online_update<D, 16>(st, s, pb, scale);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) pv_group<D>(st, pb[h], buf + Tile<D>::BYTES, 32 * j + 16 * h, lane);
+    for (int h = 0; h < 2; ++h) pv_group<D>(st, pb[h], ta.v, (32 * j + 16 * h) * TL::ROW_BYTES);
   }
 }
 
@@ -266,7 +357,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const uint16_t* __restrict__ kd, const uint16_t* __restrict__ vd, int B, int T, int Hq, int Hk, int L,
     int lgG, int nrb, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
   using TL = Tile<D>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * TL::BUF];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[2 * TL::BUF];
+  lds_u8* const smem = (lds_u8*)smem_raw;
 
   const int G = 1 << lgG;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -286,23 +378,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   g.tok_wave = (kRowsPerWave >> lgG) > 0 ? (kRowsPerWave >> lgG) : 1;
   g.key_bytes = static_cast<uint32_t>(Hk) * D * 2;
   g.tok_bytes = static_cast<uint32_t>(Hk) * (DEPTH ? L : 0) * D * 2;
-  {
-    const uint16_t* kb = k + (static_cast<int64_t>(b) * T * Hk + hk) * D;
-    const uint16_t* vb = v + (static_cast<int64_t>(b) * T * Hk + hk) * D;
-    const uint32_t seq_range = (static_cast<uint32_t>(T - 1) * Hk + 1) * D * 2;
-    g.k = make_rsrc(kb, seq_range);
-    g.v = make_rsrc(vb, seq_range);
-    if (DEPTH) {
-      const int64_t slab0 = ((static_cast<int64_t>(b) * T + tb) * Hk + hk) * static_cast<int64_t>(L) * D;
-      const int64_t range = ((static_cast<int64_t>(T - 1 - tb) * Hk + 1) * L) * D * 2;
-      const uint32_t dr = static_cast<uint32_t>(range < 0x7fffffff ? range : 0x7fffffff);
-      g.kd = make_rsrc(kd + slab0, dr);
-      g.vd = make_rsrc(vd + slab0, dr);
-    } else {
-      g.kd = g.k;
-      g.vd = g.v;
-    }
+  const uint16_t* kb = k + (static_cast<int64_t>(b) * T * Hk + hk) * D;
+  const uint16_t* vb = v + (static_cast<int64_t>(b) * T * Hk + hk) * D;
+  const uint32_t seq_range = (static_cast<uint32_t>(T - 1) * Hk + 1) * D * 2;
+  if (DEPTH) {
+    const int64_t slab0 = ((static_cast<int64_t>(b) * T + tb) * Hk + hk) * static_cast<int64_t>(L) * D;
+    const int64_t range = ((static_cast<int64_t>(T - 1 - tb) * Hk + 1) * L) * D * 2;
+    const uint32_t dr = static_cast<uint32_t>(range < 0x7fffffff ? range : 0x7fffffff);
+    g.kd = make_rsrc(kd + slab0, dr);
+    g.vd = make_rsrc(vd + slab0, dr);
   }
+  LaneOffs<D> lo;
+  init_offsets<D>(lo, lane, wave, g.key_bytes);
 
   const int wrow0 = row0 + wave * kRowsPerWave;
   const int my_row = wrow0 + r;
@@ -340,6 +427,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // wave/2, score registers [8*(wave%2), 8*(wave%2) + 8).
   const int dj = wave >> 1, dh = wave & 1;
 
+  // The LDS buffer of pipeline position pos is smem + (pos & 1) * BUF.  Its
+  // base is hidden from the optimiser so that the per-tile address adds stay
+  // in the loop instead of becoming two hoisted copies of every offset.
+  auto buf_of = [&](int pos) -> lds_u8* {
+    return smem + opaque_s((pos & 1) * TL::BUF);
+  };
+
   // ---- tile pipeline ------------------------------------------------------------
   // Sequence tiles wholly before the workgroup's first token (and the sequence
   // end) are unmasked for every wave; the few after them overlap the
@@ -352,66 +446,68 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   int pos = 0;  // pipeline position: selects the LDS buffer
   int sq = 0;   // next sequence tile
   if (DEPTH && nd > 0 && n_int / max(nd, 1) == 0)
-    dma_tile<D, true>(g, 0, nchunk, smem, wave, lane);
+    dma_depth<D>(g, 0, nchunk, smem, wave, lane);
   else
-    dma_tile<D, false>(g, 0, nchunk, smem, wave, lane);
+    dma_seq<D>(kb, vb, seq_range, g.key_bytes, Hk, 0, smem, wave, lo);
 
   if constexpr (DEPTH) {
     for (int d = 0; d < nd; ++d) {
       const int s_end = ((d + 1) * n_int) / nd;
       for (; sq < s_end; ++sq, ++pos) {
-        uint8_t* cur = smem + (pos & 1) * TL::BUF;
-        uint8_t* nxt = smem + ((pos + 1) & 1) * TL::BUF;
+        lds_u8* cur = buf_of(pos);
+        lds_u8* nxt = buf_of(pos + 1);
         publish_tile();
         if (sq + 1 < s_end)
-          dma_tile<D, false>(g, sq + 1, nchunk, nxt, wave, lane);
+          dma_seq<D>(kb, vb, seq_range, g.key_bytes, Hk, sq + 1, nxt, wave, lo);
         else
-          dma_tile<D, true>(g, d, nchunk, nxt, wave, lane);
-        seq_tile<D, false, CAUSAL>(st, qf, cur, sq * kBN, T, my_t, lane, scale_log2);
+          dma_depth<D>(g, d, nchunk, nxt, wave, lane);
+        seq_tile<D, false, CAUSAL>(st, qf, tile_addr<D>(cur, lo), sq * kBN, T, my_t, half, scale_log2);
       }
       // depth tile d: each wave sees only its own token's slots
-      uint8_t* cur = smem + (pos & 1) * TL::BUF;
-      uint8_t* nxt = smem + ((pos + 1) & 1) * TL::BUF;
+      lds_u8* cur = buf_of(pos);
+      lds_u8* nxt = buf_of(pos + 1);
       publish_tile();
       if (d + 1 < nd) {
         if (sq < ((d + 2) * n_int) / nd)
-          dma_tile<D, false>(g, sq, nchunk, nxt, wave, lane);
+          dma_seq<D>(kb, vb, seq_range, g.key_bytes, Hk, sq, nxt, wave, lo);
         else
-          dma_tile<D, true>(g, d + 1, nchunk, nxt, wave, lane);
+          dma_depth<D>(g, d + 1, nchunk, nxt, wave, lane);
       } else if (sq < ns) {
-        dma_tile<D, false>(g, sq, nchunk, nxt, wave, lane);
+        dma_seq<D>(kb, vb, seq_range, g.key_bytes, Hk, sq, nxt, wave, lo);
       }
       ++pos;
-      const f32x16 sacc = qk_block<D>(qf, cur, 32 * dj, r, half);
+      const TileAddr<D> ta = tile_addr<D>(cur, lo);
+      const f32x16 sacc = qk_block<D>(qf, ta.k, 32 * dj * TL::ROW_BYTES);
       const int dtok = d / nchunk;
       const int slot0 = (d - dtok * nchunk) * kDepthRowsPerWave;
       const bool mine = my_t == wt0 + dtok;
+      const int hf = opaque(half);
       float s[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const int slot = slot0 + 8 * (i >> 2) + 4 * half + (i & 3);
+        const int slot = slot0 + 8 * (i >> 2) + 4 * hf + (i & 3);
         s[i] = (mine && slot < L) ? sacc[8 * dh + i] : -INFINITY;
       }
       bf16x8 pb[1];
       online_update<D, 8>(st, s, pb, scale_log2);
-      pv_group<D>(st, pb[0], cur + TL::BYTES, 32 * dj + 16 * dh, lane);
+      pv_group<D>(st, pb[0], ta.v, (32 * dj + 16 * dh) * TL::ROW_BYTES);
     }
   }
   for (; sq < n_int; ++sq, ++pos) {  // unmasked sequence tiles (all of them when there is no depth)
-    uint8_t* cur = smem + (pos & 1) * TL::BUF;
-    uint8_t* nxt = smem + ((pos + 1) & 1) * TL::BUF;
+    lds_u8* cur = buf_of(pos);
+    lds_u8* nxt = buf_of(pos + 1);
     publish_tile();
-    if (sq + 1 < ns) dma_tile<D, false>(g, sq + 1, nchunk, nxt, wave, lane);
-    seq_tile<D, false, CAUSAL>(st, qf, cur, sq * kBN, T, my_t, lane, scale_log2);
+    if (sq + 1 < ns) dma_seq<D>(kb, vb, seq_range, g.key_bytes, Hk, sq + 1, nxt, wave, lo);
+    seq_tile<D, false, CAUSAL>(st, qf, tile_addr<D>(cur, lo), sq * kBN, T, my_t, half, scale_log2);
   }
   for (; sq < ns; ++sq, ++pos) {  // masked sequence tiles
-    uint8_t* cur = smem + (pos & 1) * TL::BUF;
-    uint8_t* nxt = smem + ((pos + 1) & 1) * TL::BUF;
+    lds_u8* cur = buf_of(pos);
+    lds_u8* nxt = buf_of(pos + 1);
     publish_tile();
-    if (sq + 1 < ns) dma_tile<D, false>(g, sq + 1, nchunk, nxt, wave, lane);
+    if (sq + 1 < ns) dma_seq<D>(kb, vb, seq_range, g.key_bytes, Hk, sq + 1, nxt, wave, lo);
     const int kt0 = sq * kBN;
     if (CAUSAL && kt0 > wt1) continue;  // nothing visible to this wave
-    seq_tile<D, true, CAUSAL>(st, qf, cur, kt0, T, my_t, lane, scale_log2);
+    seq_tile<D, true, CAUSAL>(st, qf, tile_addr<D>(cur, lo), kt0, T, my_t, half, scale_log2);
   }
 
   // ---- epilogue --------------------------------------------------------------
