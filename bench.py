@@ -118,6 +118,13 @@ def _sq_lines(sq_dir, command):
                          "LDS active %.4f" % (100.0 * v["SQ_VALU_MFMA_BUSY_CYCLES"] / simd_cycles,
                                               v["SQ_INSTS_VALU"] / v["SQ_INSTS_MFMA"],
                                               v["SQ_LDS_BANK_CONFLICT"] / max(1.0, v["SQ_LDS_IDX_ACTIVE"])))
+        if gui and v.get("SQ_VALU_MFMA_COEXEC_CYCLES"):
+            lines.append("    VALU issued while MFMA busy: %.1f%% of SIMD cycles"
+                         % (100.0 * v["SQ_VALU_MFMA_COEXEC_CYCLES"] / simd_cycles))
+        for name, what in (("SQ_WAIT_INST_ANY", "waiting for an instruction to issue"),
+                           ("SQ_WAIT_INST_LDS", "waiting to issue an LDS instruction")):
+            if v.get("SQ_WAVE_CYCLES") and v.get(name):  # both in quad-cycles
+                lines.append("    waves %s: %.1f%% of wave cycles" % (what, 100.0 * v[name] / v["SQ_WAVE_CYCLES"]))
     return lines
 
 
@@ -167,8 +174,8 @@ def summarize(trace_dir, fetch_dir, write_dir, command, sq_dir=None):
     alg = acc.algorithmic_bytes(shape)
     lines.append("  algorithmic bytes of the L=48 forward: %.4g B (traffic / algorithmic = %.3f)"
                  % (alg, traffic["moda_fwd_bf16 L=48"] / alg))
-    if sq_dir:
-        lines += _sq_lines(sq_dir, command[3] if len(command) > 3 else "")
+    for k, d in enumerate(sq_dir or []):
+        lines += _sq_lines(d, command[3 + k] if len(command) > 3 + k else "")
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(os.path.join(os.path.dirname(TRAFFIC_FILE), "moda_fwd_bf16_long_L48.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -188,9 +195,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write the profiles/ summary from rocprofv3 CSV output directories and exit")
-    ap.add_argument("--sq", metavar="SQ_DIR", help="with --summarize: also summarise an SQ counter pass")
+    ap.add_argument("--sq", metavar="SQ_DIR", nargs="+", help="with --summarize: also summarise SQ counter passes")
     ap.add_argument("--commands", nargs="+", default=["", "", ""],
-                    help="the rocprofv3 commands (trace, fetch, write[, sq]), for the record")
+                    help="the rocprofv3 commands (trace, fetch, write[, sq...]), for the record")
     args = ap.parse_args()
     if args.summarize:
         summarize(*args.summarize, command=args.commands, sq_dir=args.sq)

@@ -157,18 +157,53 @@ constexpr float kRescaleSlack = 8.0f;
 // plain code the multiply gets fresh destination registers and, once the
 // conditional rescale merges back, every tile pays a copy of the whole
 // accumulator; tying each element's input and output keeps it in place.
-// alpha comes straight from v_exp: the first multiply after it waits out the
-// transcendental-result hazard (inline asm is invisible to the compiler's
-// hazard checks).
-__device__ __forceinline__ void scale_in_place(f32x16& acc, float alpha, bool first) {
+// Inline asm is invisible to the compiler's hazard checks, so the waits are
+// explicit: before the first multiply, enough wait states for an MFMA result
+// (the accumulator may have been written by one shortly before) and for the
+// v_exp result alpha; after the last one, the wait a VALU result needs before
+// an MFMA reads it as its accumulator.
+__device__ __forceinline__ void scale_in_place(f32x16& acc, float alpha, bool first, bool last) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     float x = acc[i];
     if (first && i == 0)
-      asm volatile("s_nop 1\n\tv_mul_f32 %0, %0, %1" : "+v"(x) : "v"(alpha));
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\tv_mul_f32 %0, %0, %1" : "+v"(x) : "v"(alpha));
+    else if (last && i == 15)
+      asm volatile("v_mul_f32 %0, %0, %1\n\ts_nop 3" : "+v"(x) : "v"(alpha));
     else
       asm volatile("v_mul_f32 %0, %0, %1" : "+v"(x) : "v"(alpha));
     acc[i] = x;
+  }
+}
+
+// Max and sum of N values as balanced trees (three-input max steps), so the
+// dependent chain is a few instructions long rather than N.
+template <int N>
+__device__ __forceinline__ float tree_max(const float (&s)[N]) {
+  float a[(N + 2) / 3];
+#pragma unroll
+  for (int i = 0; i < (N + 2) / 3; ++i) {
+    a[i] = s[3 * i];
+    if (3 * i + 1 < N) a[i] = fmaxf(a[i], s[3 * i + 1]);
+    if (3 * i + 2 < N) a[i] = fmaxf(a[i], s[3 * i + 2]);
+  }
+  if constexpr ((N + 2) / 3 == 1) {
+    return a[0];
+  } else {
+    return tree_max<(N + 2) / 3>(a);
+  }
+}
+
+template <int N>
+__device__ __forceinline__ float tree_sum(const float (&s)[N]) {
+  static_assert((N & (N - 1)) == 0, "power of two");
+  if constexpr (N == 1) {
+    return s[0];
+  } else {
+    float a[N / 2];
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) a[i] = s[i] + s[i + N / 2];
+    return tree_sum<N / 2>(a);
   }
 }
 
@@ -176,27 +211,20 @@ __device__ __forceinline__ void scale_in_place(f32x16& acc, float alpha, bool fi
 // packed to bf16 in groups of 8 (one PV B operand per group).
 template <int D, int N>
 __device__ __forceinline__ void online_update(RowState<D>& st, float (&s)[N], bf16x8 (&pb)[N / 8], float scale) {
-  float mx = s[0];
-#pragma unroll
-  for (int i = 1; i < N; ++i) mx = fmaxf(mx, s[i]);
-  mx = pair_max(mx);
+  const float mx = pair_max(tree_max<N>(s));
   const float m_blk = mx * scale;  // -inf stays -inf (scale > 0)
   if (__any(m_blk > st.m + kRescaleSlack)) {
     const float m_new = fmaxf(st.m, m_blk);
     const float alpha = fast_exp2(st.m - (m_new == -INFINITY ? 0.0f : m_new));
     st.l *= alpha;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) scale_in_place(st.o[dt], alpha, dt == 0);
+    for (int dt = 0; dt < D / 32; ++dt) scale_in_place(st.o[dt], alpha, dt == 0, dt == D / 32 - 1);
     st.m = m_new;
   }
   const float base = (st.m == -INFINITY) ? 0.0f : st.m;
-  float sum = 0.0f;
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
-    s[i] = fast_exp2(fmaf(s[i], scale, -base));
-    sum += s[i];
-  }
-  st.l += sum;
+  for (int i = 0; i < N; ++i) s[i] = fast_exp2(fmaf(s[i], scale, -base));
+  st.l += tree_sum<N>(s);
 #pragma unroll
   for (int h = 0; h < N / 8; ++h) {
     u32x4 w;
