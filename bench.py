@@ -41,7 +41,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "moda_fwd_bf16_long_L48_traffic.js
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for name in ("moda_fwd_bf16.hip", "moda_device.h"):
+    for name in ("moda_fwd_bf16.hip", "moda_tile.h", "moda_device.h"):
         with open(os.path.join(ROOT, "depth_stream_attention_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

@@ -32,6 +32,10 @@ def load():
         fn = getattr(lib, name)
         fn.argtypes = fwd_args
         fn.restype = i32
+    lib.moda_attn_decode.argtypes = [vp] * 5 + [i32] * 6 + [vp, vp, vp, ctypes.c_size_t, vp]
+    lib.moda_attn_decode.restype = i32
+    lib.moda_attn_decode_workspace.argtypes = [i32] * 6
+    lib.moda_attn_decode_workspace.restype = ctypes.c_size_t
     lib.moda_pack_depth.argtypes = [vp, vp] + [i32] * 6 + [vp]
     lib.moda_pack_depth.restype = i32
     lib.moda_append_depth_slot.argtypes = [vp, vp] + [i32] * 7 + [vp]

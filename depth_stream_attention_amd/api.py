@@ -98,6 +98,54 @@ def moda_attn_fwd_f32(q, k_seq, v_seq, k_depth=None, v_depth=None, causal=True, 
     return _fwd("moda_attn_fwd_f32", torch.float32, q, k_seq, v_seq, k_depth, v_depth, causal, out, lse, stream)
 
 
+def moda_attn_decode_workspace(B, T, Hq, Hk, d, L):
+    """Bytes of workspace moda_attn_decode needs (0 for invalid sizes)."""
+    return int(_lib.load().moda_attn_decode_workspace(B, T, Hq, Hk, d, L))
+
+
+def moda_attn_decode(q, k_cache, v_cache, k_depth=None, v_depth=None, out=None, lse=None, workspace=None,
+                     stream=None):
+    """MoDA decode step, bf16.  q [B,Hq,d]; k_cache, v_cache [B,T,Hk,d]; k_depth, v_depth [B,Hk,L,d]
+    (the decode token's depth slab; None for L = 0).  workspace: a uint8 GPU tensor of at least
+    moda_attn_decode_workspace(...) bytes (allocated here when None).  Returns (out [B,Hq,d] bf16,
+    lse [B,Hq] fp32)."""
+    dtype = torch.bfloat16
+    _check(q, "q", dtype, 3)
+    _check(k_cache, "k_cache", dtype, 4)
+    _check(v_cache, "v_cache", dtype, 4)
+    B, Hq, d = q.shape
+    T, Hk = k_cache.shape[1], k_cache.shape[2]
+    if tuple(k_cache.shape) != (B, T, Hk, d) or tuple(v_cache.shape) != (B, T, Hk, d):
+        raise ValueError("k_cache / v_cache must be [B,T,Hk,d] = %s" % ((B, T, Hk, d),))
+    L = 0
+    if k_depth is not None and k_depth.numel() > 0:
+        _check(k_depth, "k_depth", dtype, 4)
+        _check(v_depth, "v_depth", dtype, 4)
+        L = k_depth.shape[2]
+        if tuple(k_depth.shape) != (B, Hk, L, d) or tuple(v_depth.shape) != (B, Hk, L, d):
+            raise ValueError("depth K/V must be [B,Hk,L,d] = %s" % ((B, Hk, L, d),))
+    else:
+        k_depth = v_depth = None
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _check(out, "out", dtype, 3)
+    _check(lse, "lse", torch.float32, 2)
+    if tuple(out.shape) != (B, Hq, d) or tuple(lse.shape) != (B, Hq):
+        raise ValueError("out must be [B,Hq,d] and lse [B,Hq]")
+    need = moda_attn_decode_workspace(B, T, Hq, Hk, d, L)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check(workspace, "workspace", torch.uint8, 1)
+    rc = _lib.load().moda_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_depth), _ptr(v_depth),
+                                      B, T, Hq, Hk, d, L, _ptr(out), _ptr(lse), _ptr(workspace),
+                                      workspace.numel(), _stream(stream))
+    if rc != MODA_OK:
+        raise MODAError("moda_attn_decode", rc)
+    return out, lse
+
+
 def _layout_check(t, name):
     if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
         raise ValueError("%s must be a contiguous GPU tensor" % name)

@@ -42,6 +42,28 @@ int validate_fwd(bool bf16, const void* q, const void* k, const void* v, const v
   return MODA_OK;
 }
 
+int validate_decode(const void* q, const void* k, const void* v, const void* kd, const void* vd, int B, int T,
+                    int Hq, int Hk, int d, int L, const void* out, const float* lse, const void* ws,
+                    size_t ws_bytes) {
+  if (!q || !k || !v || !out || !lse || !ws) return MODA_ERR_NULL;
+  if (L > 0 && (!kd || !vd)) return MODA_ERR_NULL;
+  if (B <= 0 || T <= 0 || Hq <= 0 || Hk <= 0 || d <= 0 || L < 0) return MODA_ERR_SHAPE;
+  if (Hq % Hk != 0) return MODA_ERR_SHAPE;
+  if (d != 64 && d != 128) return MODA_ERR_UNSUPPORTED;
+  if (!is_pow2_in(Hq / Hk, 1, 32)) return MODA_ERR_UNSUPPORTED;
+  // One chunk of keys (or the depth slab) is addressed with 32-bit byte offsets.
+  if (static_cast<int64_t>(256) * Hk * d * 2 >= (int64_t{1} << 31) ||
+      static_cast<int64_t>(L) * d * 2 >= (int64_t{1} << 31))
+    return MODA_ERR_UNSUPPORTED;
+  if (moda::decode_grid_blocks(B, T, Hk, L) > INT_MAX || static_cast<int64_t>(B) * Hq > INT_MAX)
+    return MODA_ERR_UNSUPPORTED;
+  if (ws_bytes < moda::decode_workspace_bytes(B, T, Hq, d, L)) return MODA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse) || !aligned16(ws))
+    return MODA_ERR_ALIGN;
+  if (L > 0 && (!aligned16(kd) || !aligned16(vd))) return MODA_ERR_ALIGN;
+  return MODA_OK;
+}
+
 int validate_layout(const void* src, const void* dst, int B, int T, int L, int Hk, int d, int elem_bytes) {
   if (!src || !dst) return MODA_ERR_NULL;
   if (B <= 0 || T <= 0 || L <= 0 || Hk <= 0 || d <= 0) return MODA_ERR_SHAPE;
@@ -75,6 +97,22 @@ int moda_attn_fwd_f32(const void* q, const void* k_seq, const void* v_seq, const
                       const void* v_depth, int B, int T, int Hq, int Hk, int d, int L, int causal, void* out,
                       float* lse, moda_stream_t stream) {
   return fwd_common(false, q, k_seq, v_seq, k_depth, v_depth, B, T, Hq, Hk, d, L, causal, out, lse, stream);
+}
+
+int moda_attn_decode(const void* q, const void* k_cache, const void* v_cache, const void* k_depth,
+                     const void* v_depth, int B, int T, int Hq, int Hk, int d, int L, void* out, float* lse,
+                     void* workspace, size_t workspace_bytes, moda_stream_t stream) {
+  const int rc = validate_decode(q, k_cache, v_cache, k_depth, v_depth, B, T, Hq, Hk, d, L, out, lse, workspace,
+                                 workspace_bytes);
+  if (rc != MODA_OK) return rc;
+  moda::DecodeArgs a{q, k_cache, v_cache, L > 0 ? k_depth : nullptr, L > 0 ? v_depth : nullptr,
+                     B, T, Hq, Hk, d, L, out, lse, workspace, stream};
+  return moda::launch_decode_bf16(a) == hipSuccess ? MODA_OK : MODA_ERR_HIP;
+}
+
+size_t moda_attn_decode_workspace(int B, int T, int Hq, int Hk, int d, int L) {
+  if (B <= 0 || T <= 0 || Hq <= 0 || Hk <= 0 || d <= 0 || L < 0) return 0;
+  return moda::decode_workspace_bytes(B, T, Hq, d, L);
 }
 
 int moda_pack_depth(const void* src, void* dst, int B, int T, int L, int Hk, int d, int elem_bytes,

@@ -40,8 +40,8 @@
 //     FMA; the output rescale is skipped unless a row max grows by more than
 //     2^8.  lse is converted back to the natural log at the end.
 //   * Causal workgroups are issued heaviest first (last row block first).
-#include "moda_device.h"
 #include "moda_launch.h"
+#include "moda_tile.h"
 
 namespace moda {
 namespace {
@@ -50,43 +50,11 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kRowsPerWave = 32;
 constexpr int kBM = kWaves * kRowsPerWave;  // expanded rows per workgroup
-constexpr int kBN = 64;                     // rows (keys or depth slots) per tile
 constexpr int kDepthRowsPerWave = kBN / kWaves;
 
-// LDS pointers are kept in address space 3 (32-bit) so tile addressing is
-// plain 32-bit arithmetic.
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
-typedef __attribute__((ext_vector_type(4))) short s16x4;
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
-typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8_t;
-
-// The LDS object at byte address addr.  (Built from the integer: the null
-// pointer of the LDS address space is not address 0.)
-template <typename T>
-__device__ __forceinline__ T* lds_at(uint32_t addr) {
-  return reinterpret_cast<T*>(static_cast<uintptr_t>(addr));
-}
-__device__ __forceinline__ uint32_t lds_addr(const lds_u8* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
-}
-
-// Tile geometry for head dimension D.  A tile row (one key or slot) is D*2
-// bytes = CH chunks of 16 bytes.  One DMA instruction of a wave fills 1 KiB =
-// RPI rows; each wave issues NX instructions per K (and per V) tile.
+// Direct-to-LDS load instructions per wave per K (or V) tile.
 template <int D>
-struct Tile {
-  static constexpr int ROW_BYTES = D * 2;
-  static constexpr int CH = D / 8;
-  static constexpr int RPI = 64 / CH;
-  static constexpr int NX = CH / kWaves;
-  static constexpr int BYTES = kBN * ROW_BYTES;  // one K or V tile
-  static constexpr int BUF = 2 * BYTES;          // K then V
-  static constexpr int RPB = 256 / ROW_BYTES;    // rows sharing one 256-byte bank row
-  // Chunk swizzles: logical chunk c of row r lives at physical chunk c ^ swz(r).
-  __device__ static __forceinline__ int swz_k(int row) { return (row / RPB) % CH; }
-  __device__ static __forceinline__ int swz_v(int row) { return 4 * ((row / RPB) % (CH / 4)); }
-};
+constexpr int kNX = Tile<D>::CH / kWaves;
 
 // Per-workgroup staging geometry.  All global tile reads are raw buffer loads
 // against four descriptors whose ranges end exactly at the last valid row, so
@@ -103,14 +71,6 @@ struct Geo {
   int tok_wave;         // tokens per wave (32 / G)
 };
 
-constexpr uint32_t kOutOfRange = 0x80000000u;  // > every descriptor range (host-checked)
-constexpr int kBufFlags = 0x00020000;         // raw buffer, 32-bit dwords
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint16_t* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), static_cast<short>(0),
-                                           static_cast<int>(bytes), kBufFlags);
-}
-
 // Direct-to-LDS loads of depth tile `idx` into `buf` (K at buf, V at
 // buf + BYTES).  For every wave w the tile holds token w*tok_wave + dtok of
 // the workgroup, slots [16*dch, 16*dch + 16), at tile rows [16w, 16w + 16).
@@ -124,8 +84,8 @@ __device__ __forceinline__ void dma_depth(const Geo& g, int idx, int nchunk, lds
   const int dtok = idx / nchunk;
   const int dch = idx - dtok * nchunk;
 #pragma unroll
-  for (int x = 0; x < TL::NX; ++x) {
-    const int pr = (wave * TL::NX + x) * TL::RPI + lane / TL::CH;
+  for (int x = 0; x < kNX<D>; ++x) {
+    const int pr = (wave * kNX<D> + x) * TL::RPI + lane / TL::CH;
     const int pc = lane % TL::CH;
     const int slot = dch * kDepthRowsPerWave + (pr % kDepthRowsPerWave);
     const uint32_t row_off = static_cast<uint32_t>(wave * g.tok_wave + dtok) * g.tok_bytes +
@@ -133,104 +93,9 @@ __device__ __forceinline__ void dma_depth(const Geo& g, int idx, int nchunk, lds
     const bool valid = slot < g.L;
     const uint32_t ok = valid ? row_off + ((pc ^ TL::swz_k(pr)) * 16) : kOutOfRange;  // selects, not branches
     const uint32_t ov = valid ? row_off + ((pc ^ TL::swz_v(pr)) * 16) : kOutOfRange;
-    lds_u8* dk = buf + (wave * TL::NX + x) * 1024;
+    lds_u8* dk = buf + (wave * kNX<D> + x) * 1024;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(g.kd, (lds_void_t*)dk, 16, ok, 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(g.vd, (lds_void_t*)(dk + TL::BYTES), 16, ov, 0, 0, 0);
-  }
-}
-
-// Running softmax state of one query row held by a lane pair (l, l ^ 32).
-template <int D>
-struct RowState {
-  f32x16 o[D / 32];  // O^T accumulator: d = 32*dt + 8*(i/4) + 4*half + (i%4)
-  float m;           // base-2 exponent offset of the row (same in both lanes)
-  float l;           // this lane's share of the running denominator
-};
-
-// The row's exponent offset m only moves when a block's max exceeds it by more
-// than this (base 2), so unnormalised weights stay below 2^8 and the costly
-// rescale of the output accumulator is rare.  Any offset gives the same
-// quotient; the final division and lse use the offset actually applied.
-constexpr float kRescaleSlack = 8.0f;
-
-// acc *= alpha, element by element in the accumulator's own registers.  As
-// plain code the multiply gets fresh destination registers and, once the
-// conditional rescale merges back, every tile pays a copy of the whole
-// accumulator; tying each element's input and output keeps it in place.
-// Inline asm is invisible to the compiler's hazard checks, so the waits are
-// explicit: before the first multiply, enough wait states for an MFMA result
-// (the accumulator may have been written by one shortly before) and for the
-// v_exp result alpha; after the last one, the wait a VALU result needs before
-// an MFMA reads it as its accumulator.
-__device__ __forceinline__ void scale_in_place(f32x16& acc, float alpha, bool first, bool last) {
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    float x = acc[i];
-    if (first && i == 0)
-      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\tv_mul_f32 %0, %0, %1" : "+v"(x) : "v"(alpha));
-    else if (last && i == 15)
-      asm volatile("v_mul_f32 %0, %0, %1\n\ts_nop 3" : "+v"(x) : "v"(alpha));
-    else
-      asm volatile("v_mul_f32 %0, %0, %1" : "+v"(x) : "v"(alpha));
-    acc[i] = x;
-  }
-}
-
-// Max and sum of N values as balanced trees (three-input max steps), so the
-// dependent chain is a few instructions long rather than N.
-template <int N>
-__device__ __forceinline__ float tree_max(const float (&s)[N]) {
-  float a[(N + 2) / 3];
-#pragma unroll
-  for (int i = 0; i < (N + 2) / 3; ++i) {
-    a[i] = s[3 * i];
-    if (3 * i + 1 < N) a[i] = fmaxf(a[i], s[3 * i + 1]);
-    if (3 * i + 2 < N) a[i] = fmaxf(a[i], s[3 * i + 2]);
-  }
-  if constexpr ((N + 2) / 3 == 1) {
-    return a[0];
-  } else {
-    return tree_max<(N + 2) / 3>(a);
-  }
-}
-
-template <int N>
-__device__ __forceinline__ float tree_sum(const float (&s)[N]) {
-  static_assert((N & (N - 1)) == 0, "power of two");
-  if constexpr (N == 1) {
-    return s[0];
-  } else {
-    float a[N / 2];
-#pragma unroll
-    for (int i = 0; i < N / 2; ++i) a[i] = s[i] + s[i + N / 2];
-    return tree_sum<N / 2>(a);
-  }
-}
-
-// Fold N raw scores (-inf = masked) into the state and return the weights,
-// packed to bf16 in groups of 8 (one PV B operand per group).
-template <int D, int N>
-__device__ __forceinline__ void online_update(RowState<D>& st, float (&s)[N], bf16x8 (&pb)[N / 8], float scale) {
-  const float mx = pair_max(tree_max<N>(s));
-  const float m_blk = mx * scale;  // -inf stays -inf (scale > 0)
-  if (__any(m_blk > st.m + kRescaleSlack)) {
-    const float m_new = fmaxf(st.m, m_blk);
-    const float alpha = fast_exp2(st.m - (m_new == -INFINITY ? 0.0f : m_new));
-    st.l *= alpha;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) scale_in_place(st.o[dt], alpha, dt == 0, dt == D / 32 - 1);
-    st.m = m_new;
-  }
-  const float base = (st.m == -INFINITY) ? 0.0f : st.m;
-#pragma unroll
-  for (int i = 0; i < N; ++i) s[i] = fast_exp2(fmaf(s[i], scale, -base));
-  st.l += tree_sum<N>(s);
-#pragma unroll
-  for (int h = 0; h < N / 8; ++h) {
-    u32x4 w;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) w[k] = pack_bf16x2(s[8 * h + 2 * k], s[8 * h + 2 * k + 1]);
-    pb[h] = __builtin_bit_cast(bf16x8, w);
   }
 }
 
@@ -243,7 +108,7 @@ template <int D>
 struct LaneOffs {
   uint32_t kr[D / 16];                        // K read of slice sl, tile rows 0..31 (rows 32..63: + 32 rows)
   uint32_t vr[D / 32];                        // V transposed read of d tile dt, keys 0..15 (others: + rows)
-  uint32_t dk[Tile<D>::NX], dv[Tile<D>::NX];  // sequence-tile loads, relative to the tile's first key
+  uint32_t dk[kNX<D>], dv[kNX<D>];  // sequence-tile loads, relative to the tile's first key
 };
 
 template <int D>
@@ -263,8 +128,8 @@ __device__ __forceinline__ void init_offsets(LaneOffs<D>& lo, int lane, int wave
   // Load instruction x of wave w fills tile rows pr = (w*NX + x)*RPI + lane/CH,
   // physical chunk pc = lane % CH, with logical chunk pc ^ swz(pr).
 #pragma unroll
-  for (int x = 0; x < TL::NX; ++x) {
-    const int pr = (wave * TL::NX + x) * TL::RPI + lane / TL::CH;
+  for (int x = 0; x < kNX<D>; ++x) {
+    const int pr = (wave * kNX<D> + x) * TL::RPI + lane / TL::CH;
     const int pc = lane % TL::CH;
     lo.dk[x] = static_cast<uint32_t>(pr) * key_bytes + ((pc ^ TL::swz_k(pr)) * 16);
     lo.dv[x] = static_cast<uint32_t>(pr) * key_bytes + ((pc ^ TL::swz_v(pr)) * 16);
@@ -285,43 +150,11 @@ __device__ __forceinline__ void dma_seq(const uint16_t* kb, const uint16_t* vb, 
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb + first, range);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb + first, range);
 #pragma unroll
-  for (int x = 0; x < TL::NX; ++x) {
-    lds_u8* dk = buf + (wave * TL::NX + x) * 1024;
+  for (int x = 0; x < kNX<D>; ++x) {
+    lds_u8* dk = buf + (wave * kNX<D> + x) * 1024;
     const uint32_t ok = lo.dk[x], ov = lo.dv[x];
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)dk, 16, ok, 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(dk + TL::BYTES), 16, ov, 0, 0, 0);
-  }
-}
-
-// S^T block: 32 keys x the wave's 32 query rows.  kt[sl] holds the lane's
-// read address of slice sl for the block's first row; lane l supplies key row
-// l%32, logical chunk 2*sl + l/32.
-template <int D>
-__device__ __forceinline__ f32x16 qk_block(const bf16x8 (&qf)[D / 16], const uint32_t (&kt)[D / 16], int row_bytes_off) {
-  f32x16 s = {};
-#pragma unroll
-  for (int sl = 0; sl < D / 16; ++sl) {
-    const bf16x8 a = *lds_at<lds_bf16x8_t>(kt[sl] + row_bytes_off);
-    s = mfma32(a, qf[sl], s);
-  }
-  return s;
-}
-
-// O^T += V^T * P^T for one 16-key group whose first V row is `off` bytes past
-// the addresses in vt.  The B operand pb holds, in lane half hf, the weights
-// of keys 4*hf + {0..3} and 8 + 4*hf + {0..3} of the group.  The A operand is
-// read with two transposing LDS reads: lane i of each 16-lane group points at
-// row key_b + i/4, columns d0 + 4*(i%4) .. +3, and receives V[key_b + k][d0 + i]
-// for k = 0..3.
-template <int D>
-__device__ __forceinline__ void pv_group(RowState<D>& st, const bf16x8& pb, const uint32_t (&vt)[D / 32], int off) {
-  using TL = Tile<D>;
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) {
-    const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_at<lds_s16x4_t>(vt[dt] + off));
-    const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_at<lds_s16x4_t>(vt[dt] + off + 8 * TL::ROW_BYTES));
-    const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-    st.o[dt] = mfma32(a, pb, st.o[dt]);
   }
 }
 
@@ -373,19 +206,13 @@ __device__ __forceinline__ void seq_tile(RowState<D>& st, const bf16x8 (&qf)[D /
   }
 }
 
-// Publish the tile this wave's DMA loads filled: wait for them, then barrier.
-__device__ __forceinline__ void publish_tile() {
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-  __syncthreads();
-}
-
 template <int D, bool DEPTH, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void moda_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ kd, const uint16_t* __restrict__ vd, int B, int T, int Hq, int Hk, int L,
     int lgG, int nrb, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
   using TL = Tile<D>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[2 * TL::BUF];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[4 * TL::BYTES];
   lds_u8* const smem = (lds_u8*)smem_raw;
 
   const int G = 1 << lgG;
@@ -455,11 +282,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // wave/2, score registers [8*(wave%2), 8*(wave%2) + 8).
   const int dj = wave >> 1, dh = wave & 1;
 
-  // The LDS buffer of pipeline position pos is smem + (pos & 1) * BUF.  Its
+  // The LDS buffer of pipeline position pos is smem + (pos & 1) * 2 * BYTES.  Its
   // base is hidden from the optimiser so that the per-tile address adds stay
   // in the loop instead of becoming two hoisted copies of every offset.
   auto buf_of = [&](int pos) -> lds_u8* {
-    return smem + opaque_s((pos & 1) * TL::BUF);
+    return smem + opaque_s((pos & 1) * (2 * TL::BYTES));
   };
 
   // ---- tile pipeline ------------------------------------------------------------

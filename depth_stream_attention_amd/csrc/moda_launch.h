@@ -14,10 +14,23 @@ struct FwdArgs {
   void* stream;
 };
 
+struct DecodeArgs {
+  const void *q, *k, *v, *kd, *vd;  // q [B][Hq][d]; caches [B][T][Hk][d]; depth [B][Hk][L][d]
+  int B, T, Hq, Hk, d, L;
+  void* out;   // [B][Hq][d]
+  float* lse;  // [B][Hq]
+  void* workspace;
+  void* stream;
+};
+
 hipError_t launch_fwd_bf16(const FwdArgs& a);
 hipError_t launch_fwd_f32(const FwdArgs& a);
 int64_t fwd_bf16_grid_blocks(int B, int T, int Hq, int Hk);
 int64_t fwd_f32_grid_blocks(int B, int T, int Hq);
+
+hipError_t launch_decode_bf16(const DecodeArgs& a);
+size_t decode_workspace_bytes(int B, int T, int Hq, int d, int L);
+int64_t decode_grid_blocks(int B, int T, int Hk, int L);
 
 hipError_t launch_pack_depth(const void* src, void* dst, int B, int T, int L, int Hk, int d, int elem_bytes,
                              void* stream);

@@ -25,6 +25,8 @@
 #ifndef MODA_H
 #define MODA_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -87,6 +89,54 @@ int moda_attn_fwd(const void* q, const void* k_seq, const void* v_seq, const voi
 int moda_attn_fwd_f32(const void* q, const void* k_seq, const void* v_seq, const void* k_depth,
                       const void* v_depth, int B, int T, int Hq, int Hk, int d, int L, int causal,
                       void* out, float* lse, moda_stream_t stream);
+
+/*
+ * MoDA decode step, bf16 in / bf16 out, fp32 accumulation: one new token per
+ * sequence attends jointly to the whole KV cache of its sequence and to its own
+ * L depth slots ([Summ] 2.2 MoDA; [Notes] 二.2 unified softmax; [Notes] 二.4 on
+ * the decode cost of the depth cache).  For batch b and query head h, with
+ * hk = floor(h / G) and s = 1/sqrt(d), one softmax runs over
+ *   - the T cached keys j of KV head hk, logit s * <q[b,h], k_cache[b,j,hk]>,
+ *     value v_cache[b,j,hk] (the decode token is the last of the sequence, so
+ *     every cached key is visible; its own key is expected in the cache);
+ *   - the L depth slots i, logit s * <q[b,h], k_depth[b,hk,i]>, value
+ *     v_depth[b,hk,i].
+ *   out[b,h,:] = sum(e^logit * value) / sum(e^logit);  lse[b,h] = log(sum(e^logit)).
+ * This equals row t = T-1 of moda_attn_fwd (causal) when the token's query is
+ * q[b,T-1] and its packed depth slab is k_depth[b,T-1] / v_depth[b,T-1].
+ *
+ * Arguments
+ *   q        [B][Hq][d] bf16
+ *   k_cache  [B][T][Hk][d] bf16 (the layout of moda_attn_fwd's k_seq)
+ *   v_cache  [B][T][Hk][d] bf16
+ *   k_depth  [B][Hk][L][d] bf16: the decode token's depth slab per KV head.
+ *            May be NULL iff L == 0.
+ *   v_depth  [B][Hk][L][d] bf16, same rule.
+ *   out      [B][Hq][d] bf16 (written).   lse  [B][Hq] fp32 (written).
+ *   workspace  device memory of at least moda_attn_decode_workspace(...)
+ *            bytes, owned by the caller, 16-byte aligned; holds per-chunk
+ *            partial results during the call (contents on entry are ignored,
+ *            on return unspecified).  Calls that share a workspace must not
+ *            overlap in time.
+ *   workspace_bytes  its size.
+ * The keys are reduced in chunks of 256 (plus one chunk for the depth slots)
+ * whose partial results are merged in a fixed order: results are deterministic.
+ *
+ * Errors: MODA_ERR_NULL (q, caches, out, lse or workspace NULL; depth NULL with
+ * L > 0); MODA_ERR_SHAPE (a size <= 0, L < 0, Hq % Hk != 0, or workspace_bytes
+ * below moda_attn_decode_workspace); MODA_ERR_UNSUPPORTED (d not 64 or 128; G
+ * not in {1,2,4,8,16,32}; the workgroup count or 256 * Hk * d * 2 bytes beyond
+ * 2^31); MODA_ERR_ALIGN; MODA_ERR_HIP.
+ */
+int moda_attn_decode(const void* q, const void* k_cache, const void* v_cache, const void* k_depth,
+                     const void* v_depth, int B, int T, int Hq, int Hk, int d, int L, void* out, float* lse,
+                     void* workspace, size_t workspace_bytes, moda_stream_t stream);
+
+/*
+ * Workspace bytes moda_attn_decode needs for these sizes (host only; 0 when a
+ * size is invalid).
+ */
+size_t moda_attn_decode_workspace(int B, int T, int Hq, int Hk, int d, int L);
 
 /*
  * Depth-stream pack: dst[b][t][hk][l][:] = src[b][t][l][hk][:], bit for bit.

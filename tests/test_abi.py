@@ -23,7 +23,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = _lib.declared_symbols()
     assert {"moda_attn_fwd", "moda_attn_fwd_f32", "moda_pack_depth", "moda_append_depth_slot",
-            "moda_error_string", "moda_block_span"} <= set(names)
+            "moda_error_string", "moda_block_span", "moda_attn_decode", "moda_attn_decode_workspace"} <= set(names)
     for n in names:
         assert hasattr(lib, n), "libmoda.so does not export %s" % n
 
@@ -95,3 +95,33 @@ def test_block_span_against_brute_force(lib):
         api.moda_block_span(-1, 4, 2)
     with pytest.raises(api.MODAError):
         api.moda_block_span(0, 0, 2)
+
+
+def decode(lib, q=A, kc=A, vc=A, kd=A, vd=A, B=2, T=300, Hq=8, Hk=2, d=128, L=5, out=A2, lse=A2, ws=A2,
+           ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.moda_attn_decode_workspace(B, T, Hq, Hk, d, L)
+    return lib.moda_attn_decode(q, kc, vc, kd, vd, B, T, Hq, Hk, d, L, out, lse, ws, ws_bytes, None)
+
+
+def test_decode_workspace_size(lib):
+    # 256-key chunks plus one chunk for the depth slots; (d + 2) fp32 per (b, h, chunk).
+    assert lib.moda_attn_decode_workspace(2, 300, 8, 2, 128, 5) == 2 * 8 * (2 + 1) * 130 * 4
+    assert lib.moda_attn_decode_workspace(1, 256, 4, 4, 64, 0) == 1 * 4 * 1 * 66 * 4
+    assert lib.moda_attn_decode_workspace(1, 257, 4, 4, 64, 0) == 1 * 4 * 2 * 66 * 4
+    assert lib.moda_attn_decode_workspace(0, 256, 4, 4, 64, 0) == 0
+    assert lib.moda_attn_decode_workspace(1, 256, 4, 4, 64, -1) == 0
+
+
+def test_decode_validation(lib):
+    null = ctypes.c_void_p(0)
+    for kw in (dict(q=null), dict(kc=null), dict(vc=null), dict(out=null), dict(lse=null), dict(ws=null),
+               dict(kd=null), dict(vd=null)):
+        assert decode(lib, **kw) == api.MODA_ERR_NULL, kw
+    for kw in (dict(B=0), dict(T=0), dict(Hq=0), dict(Hk=0), dict(d=0), dict(L=-1), dict(Hq=6, Hk=4)):
+        assert decode(lib, **kw) == api.MODA_ERR_SHAPE, kw
+    assert decode(lib, ws_bytes=lib.moda_attn_decode_workspace(2, 300, 8, 2, 128, 5) - 4) == api.MODA_ERR_SHAPE
+    for kw in (dict(d=96), dict(Hq=6, Hk=2), dict(Hq=128, Hk=2)):
+        assert decode(lib, **kw) == api.MODA_ERR_UNSUPPORTED, kw
+    for kw in (dict(q=MIS), dict(kc=MIS), dict(vc=MIS), dict(kd=MIS), dict(vd=MIS), dict(out=MIS), dict(ws=MIS)):
+        assert decode(lib, **kw) == api.MODA_ERR_ALIGN, kw
