@@ -98,6 +98,10 @@ def _kernel_label(name):
         return "moda_fwd_bf16 L=48" if depth == "true" else "moda_fwd_bf16 L=0"
     if "pack_kernel" in name:
         return "moda_pack_depth"
+    if "moda_decode_partial_kernel" in name:
+        return "moda_decode partial"
+    if "moda_decode_merge_kernel" in name:
+        return "moda_decode merge"
     return None
 
 
@@ -160,13 +164,21 @@ def summarize(trace_dir, fetch_dir, write_dir, command, sq_dir=None):
     F0 = acc.flops(I.workload(5, 1))
     avg48, avg0 = stats["moda_fwd_bf16 L=48"][1], stats["moda_fwd_bf16 L=0"][1]
     lines += ["", "  MoDA L=48: %.1f TFLOP/s (%.4g flop / %.4f ms); L=0: %.1f TFLOP/s; ratio %.4f" % (
-        F / avg48 / 1e9, F, avg48, F0 / avg0 / 1e9, avg48 / avg0), "",
+        F / avg48 / 1e9, F, avg48, F0 / avg0 / 1e9, avg48 / avg0)]
+    if "moda_decode partial" in stats and "moda_decode merge" in stats:
+        ds = DECODE_SHAPE
+        dbytes = acc.decode_bytes(ds["B"], ds["T"], ds["Hq"], ds["Hk"], ds["d"], ds["L"])
+        dms = stats["moda_decode partial"][1] + stats["moda_decode merge"][1]
+        lines.append("  decode step (%s): partial + merge %.4f ms, %.1f GB/s of %d algorithmic bytes "
+                     "(%.1f%% of 8 TB/s)" % (", ".join("%s=%d" % kv for kv in ds.items()), dms,
+                                             dbytes / dms / 1e6, dbytes, dbytes / dms / 1e6 / PEAK_HBM_GBS * 100))
+    lines += ["",
         "HBM traffic per launch (rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE, separate runs):",
         "  commands: " + command[1], "            " + command[2],
         "  calibration on moda_pack_depth (reads and writes %d bytes): FETCH_SIZE x %.4f, WRITE_SIZE x %.4f"
         % (pack_bytes, f_scale, w_scale), ""]
     traffic = {}
-    for lab in ("moda_fwd_bf16 L=48", "moda_fwd_bf16 L=0", "moda_pack_depth"):
+    for lab in ("moda_fwd_bf16 L=48", "moda_fwd_bf16 L=0", "moda_pack_depth", "moda_decode partial"):
         rd = counters["FETCH_SIZE"].get(lab, 0.0) * f_scale
         wr = counters["WRITE_SIZE"].get(lab, 0.0) * w_scale
         traffic[lab] = rd + wr
@@ -186,6 +198,43 @@ def summarize(trace_dir, fetch_dir, write_dir, command, sq_dir=None):
     print("\n".join(lines))
 
 
+DECODE_SHAPE = dict(B=16, T=65536, Hq=16, Hk=4, d=128, L=48)
+
+
+def decode_leg(iters=20, warmup=3):
+    """The decode step at the long-context layer's head shapes, batch 16: HBM-bound, timed with
+    HIP events on the current stream after warm-up; inputs resident in HBM."""
+    s = DECODE_SHAPE
+    B, T, Hq, Hk, d, L = s["B"], s["T"], s["Hq"], s["Hk"], s["d"], s["L"]
+    g = torch.Generator(device="cuda").manual_seed(7)
+    q = torch.randn(B, Hq, d, device="cuda", generator=g).bfloat16()
+    kc = torch.randn(B, T, Hk, d, device="cuda", generator=g).bfloat16()
+    vc = torch.randn(B, T, Hk, d, device="cuda", generator=g).bfloat16()
+    kd = torch.randn(B, Hk, L, d, device="cuda", generator=g).bfloat16()
+    vd = torch.randn(B, Hk, L, d, device="cuda", generator=g).bfloat16()
+    ws = torch.empty(api.moda_attn_decode_workspace(B, T, Hq, Hk, d, L), dtype=torch.uint8, device="cuda")
+    out = torch.empty(B, Hq, d, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(B, Hq, dtype=torch.float32, device="cuda")
+    for _ in range(warmup):
+        api.moda_attn_decode(q, kc, vc, kd, vd, out, lse, ws)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(iters):
+        api.moda_attn_decode(q, kc, vc, kd, vd, out, lse, ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    byts = acc.decode_bytes(B, T, Hq, Hk, d, L)
+    gbs = byts / (ms * 1e-3) / 1e9
+    del q, kc, vc, kd, vd, ws
+    return {"workload": "decode step B=16 T=65536 Hq=16 Hk=4 d=128 L=48 (KV cache + depth slots)",
+            "ms": round(ms, 4), "bytes": byts,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -193,6 +242,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
     ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write the profiles/ summary from rocprofv3 CSV output directories and exit")
     ap.add_argument("--sq", metavar="SQ_DIR", nargs="+", help="with --summarize: also summarise SQ counter passes")
@@ -281,6 +331,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
     }
+    if not args.no_decode:
+        rec["decode"] = decode_leg()
     if not args.no_cpu_baseline:
         host = {k: v.cpu() for k, v in dev.items()}
         cpu, rows, ref = cpu_baseline(shape, host, args.cpu_seconds)

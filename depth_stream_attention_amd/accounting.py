@@ -43,6 +43,16 @@ def algorithmic_bytes(shape) -> int:
     return q_out + kv + depth_bytes(s) + 4 * s.B * s.Hq * s.T
 
 
+def decode_bytes(B, T, Hq, Hk, d, L, e=2) -> int:
+    """Minimum bytes of one decode step: the K/V cache and the token's depth slots read
+    once, q read, out written (e bytes per element), lse written (fp32)."""
+    return 2 * B * T * Hk * d * e + 2 * B * Hk * L * d * e + 2 * B * Hq * d * e + 4 * B * Hq
+
+
+def decode_flops(B, T, Hq, d, L) -> int:
+    return 4 * d * B * Hq * (T + L)
+
+
 def depth_utilisation(layout: str, T: int = 0, C: int = 0, G: int = 1) -> float:
     """Fraction of computed depth scores that are unmasked when the depth stage is
     computed densely per query block ("Mixture-of-Depths Attention" summary,

@@ -52,12 +52,12 @@ int validate_decode(const void* q, const void* k, const void* v, const void* kd,
   if (d != 64 && d != 128) return MODA_ERR_UNSUPPORTED;
   if (!is_pow2_in(Hq / Hk, 1, 32)) return MODA_ERR_UNSUPPORTED;
   // One chunk of keys (or the depth slab) is addressed with 32-bit byte offsets.
-  if (static_cast<int64_t>(256) * Hk * d * 2 >= (int64_t{1} << 31) ||
+  if (static_cast<int64_t>(1024) * Hk * d * 2 >= (int64_t{1} << 31) ||
       static_cast<int64_t>(L) * d * 2 >= (int64_t{1} << 31))
     return MODA_ERR_UNSUPPORTED;
   if (moda::decode_grid_blocks(B, T, Hk, L) > INT_MAX || static_cast<int64_t>(B) * Hq > INT_MAX)
     return MODA_ERR_UNSUPPORTED;
-  if (ws_bytes < moda::decode_workspace_bytes(B, T, Hq, d, L)) return MODA_ERR_SHAPE;
+  if (ws_bytes < moda::decode_workspace_bytes(B, T, Hq, Hk, d, L)) return MODA_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse) || !aligned16(ws))
     return MODA_ERR_ALIGN;
   if (L > 0 && (!aligned16(kd) || !aligned16(vd))) return MODA_ERR_ALIGN;
@@ -112,7 +112,8 @@ int moda_attn_decode(const void* q, const void* k_cache, const void* v_cache, co
 
 size_t moda_attn_decode_workspace(int B, int T, int Hq, int Hk, int d, int L) {
   if (B <= 0 || T <= 0 || Hq <= 0 || Hk <= 0 || d <= 0 || L < 0) return 0;
-  return moda::decode_workspace_bytes(B, T, Hq, d, L);
+  if (Hq % Hk != 0) return 0;
+  return moda::decode_workspace_bytes(B, T, Hq, Hk, d, L);
 }
 
 int moda_pack_depth(const void* src, void* dst, int B, int T, int L, int Hk, int d, int elem_bytes,

@@ -6,8 +6,8 @@
 // cost of the depth cache).
 //
 // Split-K over the cache: workgroup (b, hk, c) reduces chunk c of the keys for
-// the G query heads of KV head hk -- chunks of kChunk sequence keys, plus one
-// chunk holding the L depth slots -- to a partial (offset m, sum l, unnormalised
+// the G query heads of KV head hk -- chunks of 128 to 1024 sequence keys (sized
+// from the problem), plus one chunk holding the L depth slots -- to a partial (offset m, sum l, unnormalised
 // o) per head in the caller's workspace.  A second kernel merges the chunks of
 // each head by their offsets (the log-sum-exp identity), in a fixed order.
 //
@@ -23,15 +23,25 @@
 namespace moda {
 namespace {
 
-constexpr int kChunk = 256;  // sequence keys per workgroup
-constexpr int kRows = 32;    // keys per LDS tile: one 32-key MFMA block
+constexpr int kRows = 32;  // keys per LDS tile: one 32-key MFMA block
 
 // Bytes of one K (or V) tile of kRows rows.
 template <int D>
 constexpr int kTileBytes = kRows * Tile<D>::ROW_BYTES;
 
-int decode_seq_chunks(int T) { return (T + kChunk - 1) / kChunk; }
-int decode_chunks(int T, int L) { return decode_seq_chunks(T) + (L > 0 ? 1 : 0); }
+// Sequence keys per workgroup: the largest of 1024, 512, 256 that still gives
+// at least 512 workgroups (fewer, longer chunks amortise each workgroup's
+// start-up and the merge; small problems need the parallelism), else 128.
+int decode_chunk(int B, int T, int Hk) {
+  for (int c = 1024; c >= 256; c >>= 1)
+    if (static_cast<int64_t>(B) * Hk * ((T + c - 1) / c) >= 512) return c;
+  return 128;
+}
+int decode_seq_chunks(int B, int T, int Hk) {
+  const int c = decode_chunk(B, T, Hk);
+  return (T + c - 1) / c;
+}
+int decode_chunks(int B, int T, int Hk, int L) { return decode_seq_chunks(B, T, Hk) + (L > 0 ? 1 : 0); }
 
 // Direct-to-LDS loads of the K and V rows [first, first + kRows) of one chunk
 // into buf (K at buf, V at buf + kTileBytes).  One wave loads the whole tile:
@@ -63,7 +73,7 @@ template <int D>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 4))) void moda_decode_partial_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const uint16_t* __restrict__ kd, const uint16_t* __restrict__ vd, int T, int Hq, int Hk, int L, int lgG,
-    int nc_seq, float scale_log2, float* __restrict__ ws_o, float* __restrict__ ws_ml) {
+    int chunk, int nc_seq, float scale_log2, float* __restrict__ ws_o, float* __restrict__ ws_ml) {
   using TL = Tile<D>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[4 * kTileBytes<D>];  // two (K, V) tile buffers
   lds_u8* const smem = (lds_u8*)smem_raw;
@@ -89,12 +99,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 4))) void
     stride = D * 2;
     nkeys = L;
   } else {
-    const int key0 = c * kChunk;
+    const int key0 = c * chunk;
     const int64_t first = (static_cast<int64_t>(b) * T + key0) * Hk * D + static_cast<int64_t>(hk) * D;
     kbase = kc + first;
     vbase = vc + first;
     stride = static_cast<uint32_t>(Hk) * D * 2;
-    nkeys = min(kChunk, T - key0);
+    nkeys = min(chunk, T - key0);
   }
   const uint32_t range = static_cast<uint32_t>(nkeys - 1) * stride + D * 2;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase, range);
@@ -249,8 +259,9 @@ __global__ __launch_bounds__(kMergeWaves * 64) void moda_decode_merge_kernel(
 template <int D>
 hipError_t launch_decode_d(const DecodeArgs& a) {
   const int lgG = __builtin_ctz(a.Hq / a.Hk);
-  const int nc_seq = decode_seq_chunks(a.T);
-  const int nc = decode_chunks(a.T, a.L);
+  const int chunk = decode_chunk(a.B, a.T, a.Hk);
+  const int nc_seq = decode_seq_chunks(a.B, a.T, a.Hk);
+  const int nc = decode_chunks(a.B, a.T, a.Hk, a.L);
   const float scale_log2 = kLog2e / sqrtf(static_cast<float>(D));
   float* ws_o = static_cast<float*>(a.workspace);
   float* ws_ml = ws_o + static_cast<int64_t>(a.B) * a.Hq * nc * D;
@@ -258,7 +269,7 @@ hipError_t launch_decode_d(const DecodeArgs& a) {
                      static_cast<hipStream_t>(a.stream), static_cast<const uint16_t*>(a.q),
                      static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
                      static_cast<const uint16_t*>(a.kd), static_cast<const uint16_t*>(a.vd), a.T, a.Hq, a.Hk, a.L,
-                     lgG, nc_seq, scale_log2, ws_o, ws_ml);
+                     lgG, chunk, nc_seq, scale_log2, ws_o, ws_ml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((moda_decode_merge_kernel<D>), dim3(static_cast<unsigned>(a.B * a.Hq)),
@@ -269,12 +280,12 @@ hipError_t launch_decode_d(const DecodeArgs& a) {
 
 }  // namespace
 
-size_t decode_workspace_bytes(int B, int T, int Hq, int d, int L) {
-  return static_cast<size_t>(B) * Hq * decode_chunks(T, L) * (d + 2) * sizeof(float);
+size_t decode_workspace_bytes(int B, int T, int Hq, int Hk, int d, int L) {
+  return static_cast<size_t>(B) * Hq * decode_chunks(B, T, Hk, L) * (d + 2) * sizeof(float);
 }
 
 int64_t decode_grid_blocks(int B, int T, int Hk, int L) {
-  return static_cast<int64_t>(B) * Hk * decode_chunks(T, L);
+  return static_cast<int64_t>(B) * Hk * decode_chunks(B, T, Hk, L);
 }
 
 hipError_t launch_decode_bf16(const DecodeArgs& a) {

@@ -29,7 +29,7 @@ int64_t fwd_bf16_grid_blocks(int B, int T, int Hq, int Hk);
 int64_t fwd_f32_grid_blocks(int B, int T, int Hq);
 
 hipError_t launch_decode_bf16(const DecodeArgs& a);
-size_t decode_workspace_bytes(int B, int T, int Hq, int d, int L);
+size_t decode_workspace_bytes(int B, int T, int Hq, int Hk, int d, int L);
 int64_t decode_grid_blocks(int B, int T, int Hk, int L);
 
 hipError_t launch_pack_depth(const void* src, void* dst, int B, int T, int L, int Hk, int d, int elem_bytes,

@@ -119,13 +119,14 @@ int moda_attn_fwd_f32(const void* q, const void* k_seq, const void* v_seq, const
  *            on return unspecified).  Calls that share a workspace must not
  *            overlap in time.
  *   workspace_bytes  its size.
- * The keys are reduced in chunks of 256 (plus one chunk for the depth slots)
- * whose partial results are merged in a fixed order: results are deterministic.
+ * The keys are reduced in chunks of 128 to 1024 (chosen from B, T and Hk), plus
+ * one chunk for the depth slots, whose partial results are merged in a fixed
+ * order: results are deterministic.
  *
  * Errors: MODA_ERR_NULL (q, caches, out, lse or workspace NULL; depth NULL with
  * L > 0); MODA_ERR_SHAPE (a size <= 0, L < 0, Hq % Hk != 0, or workspace_bytes
  * below moda_attn_decode_workspace); MODA_ERR_UNSUPPORTED (d not 64 or 128; G
- * not in {1,2,4,8,16,32}; the workgroup count or 256 * Hk * d * 2 bytes beyond
+ * not in {1,2,4,8,16,32}; the workgroup count or 1024 * Hk * d * 2 bytes beyond
  * 2^31); MODA_ERR_ALIGN; MODA_ERR_HIP.
  */
 int moda_attn_decode(const void* q, const void* k_cache, const void* v_cache, const void* k_depth,
@@ -134,7 +135,7 @@ int moda_attn_decode(const void* q, const void* k_cache, const void* v_cache, co
 
 /*
  * Workspace bytes moda_attn_decode needs for these sizes (host only; 0 when a
- * size is invalid).
+ * size is invalid): (d + 2) fp32 values per (batch, query head, chunk).
  */
 size_t moda_attn_decode_workspace(int B, int T, int Hq, int Hk, int d, int L);
 

@@ -105,12 +105,16 @@ def decode(lib, q=A, kc=A, vc=A, kd=A, vd=A, B=2, T=300, Hq=8, Hk=2, d=128, L=5,
 
 
 def test_decode_workspace_size(lib):
-    # 256-key chunks plus one chunk for the depth slots; (d + 2) fp32 per (b, h, chunk).
-    assert lib.moda_attn_decode_workspace(2, 300, 8, 2, 128, 5) == 2 * 8 * (2 + 1) * 130 * 4
-    assert lib.moda_attn_decode_workspace(1, 256, 4, 4, 64, 0) == 1 * 4 * 1 * 66 * 4
-    assert lib.moda_attn_decode_workspace(1, 257, 4, 4, 64, 0) == 1 * 4 * 2 * 66 * 4
+    # (d + 2) fp32 per (b, h, chunk).  Chunks: the largest of 1024/512/256 keys giving at
+    # least 512 workgroups over B*Hk, else 128; plus one chunk for the depth slots when L > 0.
+    assert lib.moda_attn_decode_workspace(2, 300, 8, 2, 128, 5) == 2 * 8 * (3 + 1) * 130 * 4
+    assert lib.moda_attn_decode_workspace(1, 256, 4, 4, 64, 0) == 1 * 4 * 2 * 66 * 4
+    assert lib.moda_attn_decode_workspace(1, 257, 4, 4, 64, 0) == 1 * 4 * 3 * 66 * 4
+    assert lib.moda_attn_decode_workspace(16, 65536, 16, 4, 128, 48) == 16 * 16 * (64 + 1) * 130 * 4
+    assert lib.moda_attn_decode_workspace(1, 65536, 16, 4, 128, 48) == 16 * (128 + 1) * 130 * 4
     assert lib.moda_attn_decode_workspace(0, 256, 4, 4, 64, 0) == 0
     assert lib.moda_attn_decode_workspace(1, 256, 4, 4, 64, -1) == 0
+    assert lib.moda_attn_decode_workspace(1, 256, 6, 4, 64, 0) == 0
 
 
 def test_decode_validation(lib):

@@ -31,3 +31,10 @@ def test_long_context_figures():
     assert abs(acc.flops_seq(s.B, s.T, s.Hq, s.d) - 1.759e13) / 1.759e13 < 1e-3
     assert abs(acc.flops_depth(s.B, s.T, s.Hq, s.d, s.L) - 2.58e10) / 2.58e10 < 1e-2
     assert abs(acc.depth_bytes(s) - 6.44e9) / 6.44e9 < 1e-2
+
+
+def test_decode_bytes_and_flops():
+    # B=2, T=10, Hq=8, Hk=2, d=4, L=3, bf16: K and V caches 2*(2*10*2*4)*2 = 640, depth slots
+    # 2*(2*2*3*4)*2 = 192, q and out 2*(2*8*4)*2 = 256, lse 4*(2*8) = 64.
+    assert acc.decode_bytes(2, 10, 8, 2, 4, 3) == 640 + 192 + 256 + 64
+    assert acc.decode_flops(2, 10, 8, 4, 3) == 4 * 4 * 2 * 8 * 13

@@ -35,9 +35,16 @@ def decode_case(shape, seed, workspace=None):
     return check(shape, got_out, got_lse, ref_out, ref_lse, "decode")
 
 
-@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 255, 256, 257, 1000])
+@pytest.mark.parametrize("T", [1, 2, 31, 32, 33, 127, 128, 129, 255, 256, 257, 1000])
 def test_decode_cache_lengths(T):
+    # B*Hk = 4 workgroups per chunk index: the smallest (128-key) chunks.
     decode_case(S(2, T, 8, 2, 128, 5), 500 + T)
+
+
+@pytest.mark.parametrize("B,T,Hk", [(1, 33000, 4), (2, 33000, 4), (8, 16389, 4)])
+def test_decode_chunk_sizes(B, T, Hk):
+    """Shapes that select 256-, 512- and 1024-key chunks, each with a ragged last chunk."""
+    decode_case(S(B, T, 4 * Hk, Hk, 128, 6), 550 + B)
 
 
 @pytest.mark.parametrize("L", [0, 1, 16, 48, 65, 200])
