@@ -132,6 +132,32 @@ def _sq_lines(sq_dir, command):
     return lines
 
 
+def _decode_summary(stats, counters, f_scale, w_scale, command):
+    """profiles/moda_decode_b16_t64k.txt: the decode step of the same bench run."""
+    ds = DECODE_SHAPE
+    dbytes = acc.decode_bytes(ds["B"], ds["T"], ds["Hq"], ds["Hk"], ds["d"], ds["L"])
+    lines = ["# rocprofv3 summary: MoDA decode step, B=%d T=%d Hq=%d Hk=%d d=%d L=%d, bf16"
+             % (ds["B"], ds["T"], ds["Hq"], ds["Hk"], ds["d"], ds["L"]), "",
+             "kernel trace (rocprofv3 --kernel-trace --stats):", "  command: " + command[0], "",
+             "  %-22s %6s %12s %12s %12s" % ("kernel", "calls", "avg ms", "min ms", "max ms")]
+    for lab in ("moda_decode partial", "moda_decode merge"):
+        n, avg, mn, mx = stats[lab]
+        lines.append("  %-22s %6d %12.4f %12.4f %12.4f" % (lab, n, avg, mn, mx))
+    dms = stats["moda_decode partial"][1] + stats["moda_decode merge"][1]
+    lines += ["", "  decode step: partial + merge %.4f ms; %d algorithmic bytes -> %.1f GB/s (%.1f%% of 8 TB/s)"
+              % (dms, dbytes, dbytes / dms / 1e6, dbytes / dms / 1e6 / PEAK_HBM_GBS * 100), "",
+              "HBM traffic per launch (FETCH_SIZE / WRITE_SIZE passes of the same commands, calibrated on the",
+              "depth packer: FETCH_SIZE x %.4f, WRITE_SIZE x %.4f):" % (f_scale, w_scale),
+              "  commands: " + command[1], "            " + command[2], ""]
+    for lab in ("moda_decode partial", "moda_decode merge"):
+        rd = counters["FETCH_SIZE"].get(lab, 0.0) * f_scale
+        wr = counters["WRITE_SIZE"].get(lab, 0.0) * w_scale
+        lines.append("  %-22s read %.4g B  write %.4g B" % (lab, rd, wr))
+    with open(os.path.join(os.path.dirname(TRAFFIC_FILE), "moda_decode_b16_t64k.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def summarize(trace_dir, fetch_dir, write_dir, command, sq_dir=None):
     """Turn rocprofv3 CSVs of this benchmark into the committed summary and traffic record.
 
@@ -165,20 +191,13 @@ def summarize(trace_dir, fetch_dir, write_dir, command, sq_dir=None):
     avg48, avg0 = stats["moda_fwd_bf16 L=48"][1], stats["moda_fwd_bf16 L=0"][1]
     lines += ["", "  MoDA L=48: %.1f TFLOP/s (%.4g flop / %.4f ms); L=0: %.1f TFLOP/s; ratio %.4f" % (
         F / avg48 / 1e9, F, avg48, F0 / avg0 / 1e9, avg48 / avg0)]
-    if "moda_decode partial" in stats and "moda_decode merge" in stats:
-        ds = DECODE_SHAPE
-        dbytes = acc.decode_bytes(ds["B"], ds["T"], ds["Hq"], ds["Hk"], ds["d"], ds["L"])
-        dms = stats["moda_decode partial"][1] + stats["moda_decode merge"][1]
-        lines.append("  decode step (%s): partial + merge %.4f ms, %.1f GB/s of %d algorithmic bytes "
-                     "(%.1f%% of 8 TB/s)" % (", ".join("%s=%d" % kv for kv in ds.items()), dms,
-                                             dbytes / dms / 1e6, dbytes, dbytes / dms / 1e6 / PEAK_HBM_GBS * 100))
     lines += ["",
         "HBM traffic per launch (rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE, separate runs):",
         "  commands: " + command[1], "            " + command[2],
         "  calibration on moda_pack_depth (reads and writes %d bytes): FETCH_SIZE x %.4f, WRITE_SIZE x %.4f"
         % (pack_bytes, f_scale, w_scale), ""]
     traffic = {}
-    for lab in ("moda_fwd_bf16 L=48", "moda_fwd_bf16 L=0", "moda_pack_depth", "moda_decode partial"):
+    for lab in ("moda_fwd_bf16 L=48", "moda_fwd_bf16 L=0", "moda_pack_depth"):
         rd = counters["FETCH_SIZE"].get(lab, 0.0) * f_scale
         wr = counters["WRITE_SIZE"].get(lab, 0.0) * w_scale
         traffic[lab] = rd + wr
@@ -191,6 +210,8 @@ def summarize(trace_dir, fetch_dir, write_dir, command, sq_dir=None):
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(os.path.join(os.path.dirname(TRAFFIC_FILE), "moda_fwd_bf16_long_L48.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
+    if "moda_decode partial" in stats and "moda_decode merge" in stats:
+        _decode_summary(stats, counters, f_scale, w_scale, command)
     with open(TRAFFIC_FILE, "w") as f:
         json.dump({"kernel": "moda_fwd_bf16 L=48", "kernel_source_hash": kernel_source_hash(),
                    "hbm_bytes_per_launch": traffic["moda_fwd_bf16 L=48"],
