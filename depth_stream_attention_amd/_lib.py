@@ -32,6 +32,10 @@ def load():
         fn = getattr(lib, name)
         fn.argtypes = fwd_args
         fn.restype = i32
+    lib.moda_attn_fwd_ring.argtypes = [vp] * 5 + [i32] * 8 + [vp, vp, vp]
+    lib.moda_attn_fwd_ring.restype = i32
+    lib.moda_attn_decode_ring.argtypes = [vp] * 5 + [i32] * 7 + [vp, vp, vp, ctypes.c_size_t, vp]
+    lib.moda_attn_decode_ring.restype = i32
     lib.moda_attn_decode.argtypes = [vp] * 5 + [i32] * 6 + [vp, vp, vp, ctypes.c_size_t, vp]
     lib.moda_attn_decode.restype = i32
     lib.moda_attn_decode_workspace.argtypes = [i32] * 6

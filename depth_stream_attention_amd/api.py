@@ -54,7 +54,7 @@ def _check(t, name, dtype, ndim):
         raise ValueError("%s must be contiguous" % name)
 
 
-def _fwd(fn_name, dtype, q, k_seq, v_seq, k_depth, v_depth, causal, out, lse, stream):
+def _fwd(fn_name, dtype, q, k_seq, v_seq, k_depth, v_depth, causal, out, lse, stream, ring_L=None):
     _check(q, "q", dtype, 4)
     _check(k_seq, "k_seq", dtype, 4)
     _check(v_seq, "v_seq", dtype, 4)
@@ -71,6 +71,11 @@ def _fwd(fn_name, dtype, q, k_seq, v_seq, k_depth, v_depth, causal, out, lse, st
             raise ValueError("packed depth K/V must be [B,T,Hk,L,d] = %s" % ((B, T, Hk, L, d),))
     else:
         k_depth = v_depth = None
+    S = L
+    if ring_L is not None:
+        if not 0 <= ring_L <= S:
+            raise ValueError("ring: need 0 <= L <= S = %d, got L = %d" % (S, ring_L))
+        L = int(ring_L)
     if out is None:
         out = torch.empty((B, T, Hq, d), dtype=dtype, device=q.device)
     if lse is None:
@@ -79,9 +84,9 @@ def _fwd(fn_name, dtype, q, k_seq, v_seq, k_depth, v_depth, causal, out, lse, st
     _check(lse, "lse", torch.float32, 3)
     if tuple(out.shape) != (B, T, Hq, d) or tuple(lse.shape) != (B, Hq, T):
         raise ValueError("out must be [B,T,Hq,d] and lse [B,Hq,T]")
+    sizes = (B, T, Hq, Hk, d, S, L) if ring_L is not None else (B, T, Hq, Hk, d, L)
     rc = getattr(_lib.load(), fn_name)(_ptr(q), _ptr(k_seq), _ptr(v_seq), _ptr(k_depth), _ptr(v_depth),
-                                       B, T, Hq, Hk, d, L, int(bool(causal)), _ptr(out), _ptr(lse),
-                                       _stream(stream))
+                                       *sizes, int(bool(causal)), _ptr(out), _ptr(lse), _stream(stream))
     if rc != MODA_OK:
         raise MODAError(fn_name, rc)
     return out, lse
@@ -91,6 +96,13 @@ def moda_attn_fwd(q, k_seq, v_seq, k_depth=None, v_depth=None, causal=True, out=
     """MoDA forward, bf16.  q [B,T,Hq,d]; k_seq, v_seq [B,T,Hk,d]; k_depth, v_depth packed
     [B,T,Hk,L,d] (None for L = 0).  Returns (out [B,T,Hq,d] bf16, lse [B,Hq,T] fp32)."""
     return _fwd("moda_attn_fwd", torch.bfloat16, q, k_seq, v_seq, k_depth, v_depth, causal, out, lse, stream)
+
+
+def moda_attn_fwd_ring(q, k_seq, v_seq, k_depth, v_depth, L, causal=True, out=None, lse=None, stream=None):
+    """MoDA forward over a bounded depth cache: k_depth, v_depth are [B,T,Hk,S,d] ring slots, of which
+    the first L <= S are attended.  Returns (out, lse) as moda_attn_fwd."""
+    return _fwd("moda_attn_fwd_ring", torch.bfloat16, q, k_seq, v_seq, k_depth, v_depth, causal, out, lse,
+                stream, ring_L=L)
 
 
 def moda_attn_fwd_f32(q, k_seq, v_seq, k_depth=None, v_depth=None, causal=True, out=None, lse=None, stream=None):
@@ -103,8 +115,15 @@ def moda_attn_decode_workspace(B, T, Hq, Hk, d, L):
     return int(_lib.load().moda_attn_decode_workspace(B, T, Hq, Hk, d, L))
 
 
+def moda_attn_decode_ring(q, k_cache, v_cache, k_depth, v_depth, L, out=None, lse=None, workspace=None,
+                          stream=None):
+    """Decode step over a bounded depth cache: k_depth, v_depth are [B,Hk,S,d] ring slots, of which the
+    first L <= S are attended.  Returns (out, lse) as moda_attn_decode."""
+    return moda_attn_decode(q, k_cache, v_cache, k_depth, v_depth, out, lse, workspace, stream, ring_L=L)
+
+
 def moda_attn_decode(q, k_cache, v_cache, k_depth=None, v_depth=None, out=None, lse=None, workspace=None,
-                     stream=None):
+                     stream=None, ring_L=None):
     """MoDA decode step, bf16.  q [B,Hq,d]; k_cache, v_cache [B,T,Hk,d]; k_depth, v_depth [B,Hk,L,d]
     (the decode token's depth slab; None for L = 0).  workspace: a uint8 GPU tensor of at least
     moda_attn_decode_workspace(...) bytes (allocated here when None).  Returns (out [B,Hq,d] bf16,
@@ -126,6 +145,11 @@ def moda_attn_decode(q, k_cache, v_cache, k_depth=None, v_depth=None, out=None, 
             raise ValueError("depth K/V must be [B,Hk,L,d] = %s" % ((B, Hk, L, d),))
     else:
         k_depth = v_depth = None
+    S = L
+    if ring_L is not None:
+        if not 0 <= ring_L <= S:
+            raise ValueError("ring: need 0 <= L <= S = %d, got L = %d" % (S, ring_L))
+        L = int(ring_L)
     if out is None:
         out = torch.empty((B, Hq, d), dtype=dtype, device=q.device)
     if lse is None:
@@ -138,11 +162,17 @@ def moda_attn_decode(q, k_cache, v_cache, k_depth=None, v_depth=None, out=None, 
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     _check(workspace, "workspace", torch.uint8, 1)
-    rc = _lib.load().moda_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_depth), _ptr(v_depth),
-                                      B, T, Hq, Hk, d, L, _ptr(out), _ptr(lse), _ptr(workspace),
-                                      workspace.numel(), _stream(stream))
+    lib = _lib.load()
+    if ring_L is not None:
+        rc = lib.moda_attn_decode_ring(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_depth), _ptr(v_depth),
+                                       B, T, Hq, Hk, d, S, L, _ptr(out), _ptr(lse), _ptr(workspace),
+                                       workspace.numel(), _stream(stream))
+    else:
+        rc = lib.moda_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_depth), _ptr(v_depth),
+                                  B, T, Hq, Hk, d, L, _ptr(out), _ptr(lse), _ptr(workspace),
+                                  workspace.numel(), _stream(stream))
     if rc != MODA_OK:
-        raise MODAError("moda_attn_decode", rc)
+        raise MODAError("moda_attn_decode_ring" if ring_L is not None else "moda_attn_decode", rc)
     return out, lse
 
 

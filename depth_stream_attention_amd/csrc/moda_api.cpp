@@ -19,10 +19,10 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool is_pow2_in(int x, int lo, int hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }
 
 int validate_fwd(bool bf16, const void* q, const void* k, const void* v, const void* kd, const void* vd, int B, int T,
-                 int Hq, int Hk, int d, int L, int causal, const void* out, const float* lse) {
+                 int Hq, int Hk, int d, int Lcap, int L, int causal, const void* out, const float* lse) {
   if (!q || !k || !v || !out || !lse) return MODA_ERR_NULL;
   if (L > 0 && (!kd || !vd)) return MODA_ERR_NULL;
-  if (B <= 0 || T <= 0 || Hq <= 0 || Hk <= 0 || d <= 0 || L < 0) return MODA_ERR_SHAPE;
+  if (B <= 0 || T <= 0 || Hq <= 0 || Hk <= 0 || d <= 0 || L < 0 || Lcap < L) return MODA_ERR_SHAPE;
   if (Hq % Hk != 0) return MODA_ERR_SHAPE;
   if (causal != 0 && causal != 1) return MODA_ERR_SHAPE;
   if (d != 64 && d != 128) return MODA_ERR_UNSUPPORTED;
@@ -35,7 +35,7 @@ int validate_fwd(bool bf16, const void* q, const void* k, const void* v, const v
   // The bf16 kernel addresses one (batch, KV head) sequence and one
   // workgroup's depth slabs (at most 128 tokens) with 32-bit byte offsets.
   if (bf16 && (static_cast<int64_t>(T + 64) * Hk * d * 2 >= (int64_t{1} << 31) ||
-               static_cast<int64_t>(129) * Hk * L * d * 2 >= (int64_t{1} << 31)))
+               static_cast<int64_t>(129) * Hk * Lcap * d * 2 >= (int64_t{1} << 31)))
     return MODA_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse)) return MODA_ERR_ALIGN;
   if (L > 0 && (!aligned16(kd) || !aligned16(vd))) return MODA_ERR_ALIGN;
@@ -43,17 +43,17 @@ int validate_fwd(bool bf16, const void* q, const void* k, const void* v, const v
 }
 
 int validate_decode(const void* q, const void* k, const void* v, const void* kd, const void* vd, int B, int T,
-                    int Hq, int Hk, int d, int L, const void* out, const float* lse, const void* ws,
+                    int Hq, int Hk, int d, int Lcap, int L, const void* out, const float* lse, const void* ws,
                     size_t ws_bytes) {
   if (!q || !k || !v || !out || !lse || !ws) return MODA_ERR_NULL;
   if (L > 0 && (!kd || !vd)) return MODA_ERR_NULL;
-  if (B <= 0 || T <= 0 || Hq <= 0 || Hk <= 0 || d <= 0 || L < 0) return MODA_ERR_SHAPE;
+  if (B <= 0 || T <= 0 || Hq <= 0 || Hk <= 0 || d <= 0 || L < 0 || Lcap < L) return MODA_ERR_SHAPE;
   if (Hq % Hk != 0) return MODA_ERR_SHAPE;
   if (d != 64 && d != 128) return MODA_ERR_UNSUPPORTED;
   if (!is_pow2_in(Hq / Hk, 1, 32)) return MODA_ERR_UNSUPPORTED;
   // One chunk of keys (or the depth slab) is addressed with 32-bit byte offsets.
   if (static_cast<int64_t>(1024) * Hk * d * 2 >= (int64_t{1} << 31) ||
-      static_cast<int64_t>(L) * d * 2 >= (int64_t{1} << 31))
+      static_cast<int64_t>(B) * Hk * Lcap * d * 2 >= (int64_t{1} << 62))
     return MODA_ERR_UNSUPPORTED;
   if (moda::decode_grid_blocks(B, T, Hk, L) > INT_MAX || static_cast<int64_t>(B) * Hq > INT_MAX)
     return MODA_ERR_UNSUPPORTED;
@@ -75,12 +75,24 @@ int validate_layout(const void* src, const void* dst, int B, int T, int L, int H
 }
 
 int fwd_common(bool bf16, const void* q, const void* k, const void* v, const void* kd, const void* vd, int B, int T,
-               int Hq, int Hk, int d, int L, int causal, void* out, float* lse, moda_stream_t stream) {
-  const int rc = validate_fwd(bf16, q, k, v, kd, vd, B, T, Hq, Hk, d, L, causal, out, lse);
+               int Hq, int Hk, int d, int Lcap, int L, int causal, void* out, float* lse, moda_stream_t stream) {
+  const int rc = validate_fwd(bf16, q, k, v, kd, vd, B, T, Hq, Hk, d, Lcap, L, causal, out, lse);
   if (rc != MODA_OK) return rc;
-  moda::FwdArgs a{q, k, v, L > 0 ? kd : nullptr, L > 0 ? vd : nullptr, B, T, Hq, Hk, d, L, causal, out, lse, stream};
+  moda::FwdArgs a{q, k, v, L > 0 ? kd : nullptr, L > 0 ? vd : nullptr, B, T, Hq, Hk, d, L, causal, Lcap,
+                  out, lse, stream};
   const hipError_t e = bf16 ? moda::launch_fwd_bf16(a) : moda::launch_fwd_f32(a);
   return e == hipSuccess ? MODA_OK : MODA_ERR_HIP;
+}
+
+int decode_common(const void* q, const void* k_cache, const void* v_cache, const void* k_depth, const void* v_depth,
+                  int B, int T, int Hq, int Hk, int d, int S, int L, void* out, float* lse, void* workspace,
+                  size_t workspace_bytes, moda_stream_t stream) {
+  const int rc = validate_decode(q, k_cache, v_cache, k_depth, v_depth, B, T, Hq, Hk, d, S, L, out, lse, workspace,
+                                 workspace_bytes);
+  if (rc != MODA_OK) return rc;
+  moda::DecodeArgs a{q, k_cache, v_cache, L > 0 ? k_depth : nullptr, L > 0 ? v_depth : nullptr,
+                     B, T, Hq, Hk, d, L, S, out, lse, workspace, stream};
+  return moda::launch_decode_bf16(a) == hipSuccess ? MODA_OK : MODA_ERR_HIP;
 }
 
 }  // namespace
@@ -90,24 +102,33 @@ extern "C" {
 int moda_attn_fwd(const void* q, const void* k_seq, const void* v_seq, const void* k_depth, const void* v_depth,
                   int B, int T, int Hq, int Hk, int d, int L, int causal, void* out, float* lse,
                   moda_stream_t stream) {
-  return fwd_common(true, q, k_seq, v_seq, k_depth, v_depth, B, T, Hq, Hk, d, L, causal, out, lse, stream);
+  return fwd_common(true, q, k_seq, v_seq, k_depth, v_depth, B, T, Hq, Hk, d, L, L, causal, out, lse, stream);
+}
+
+int moda_attn_fwd_ring(const void* q, const void* k_seq, const void* v_seq, const void* k_depth,
+                       const void* v_depth, int B, int T, int Hq, int Hk, int d, int S, int L, int causal,
+                       void* out, float* lse, moda_stream_t stream) {
+  return fwd_common(true, q, k_seq, v_seq, k_depth, v_depth, B, T, Hq, Hk, d, S, L, causal, out, lse, stream);
 }
 
 int moda_attn_fwd_f32(const void* q, const void* k_seq, const void* v_seq, const void* k_depth,
                       const void* v_depth, int B, int T, int Hq, int Hk, int d, int L, int causal, void* out,
                       float* lse, moda_stream_t stream) {
-  return fwd_common(false, q, k_seq, v_seq, k_depth, v_depth, B, T, Hq, Hk, d, L, causal, out, lse, stream);
+  return fwd_common(false, q, k_seq, v_seq, k_depth, v_depth, B, T, Hq, Hk, d, L, L, causal, out, lse, stream);
 }
 
 int moda_attn_decode(const void* q, const void* k_cache, const void* v_cache, const void* k_depth,
                      const void* v_depth, int B, int T, int Hq, int Hk, int d, int L, void* out, float* lse,
                      void* workspace, size_t workspace_bytes, moda_stream_t stream) {
-  const int rc = validate_decode(q, k_cache, v_cache, k_depth, v_depth, B, T, Hq, Hk, d, L, out, lse, workspace,
-                                 workspace_bytes);
-  if (rc != MODA_OK) return rc;
-  moda::DecodeArgs a{q, k_cache, v_cache, L > 0 ? k_depth : nullptr, L > 0 ? v_depth : nullptr,
-                     B, T, Hq, Hk, d, L, out, lse, workspace, stream};
-  return moda::launch_decode_bf16(a) == hipSuccess ? MODA_OK : MODA_ERR_HIP;
+  return decode_common(q, k_cache, v_cache, k_depth, v_depth, B, T, Hq, Hk, d, L, L, out, lse, workspace,
+                       workspace_bytes, stream);
+}
+
+int moda_attn_decode_ring(const void* q, const void* k_cache, const void* v_cache, const void* k_depth,
+                          const void* v_depth, int B, int T, int Hq, int Hk, int d, int S, int L, void* out,
+                          float* lse, void* workspace, size_t workspace_bytes, moda_stream_t stream) {
+  return decode_common(q, k_cache, v_cache, k_depth, v_depth, B, T, Hq, Hk, d, S, L, out, lse, workspace,
+                       workspace_bytes, stream);
 }
 
 size_t moda_attn_decode_workspace(int B, int T, int Hq, int Hk, int d, int L) {

@@ -72,8 +72,8 @@ __device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t rk, __amdgpu_buf
 template <int D>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 4))) void moda_decode_partial_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
-    const uint16_t* __restrict__ kd, const uint16_t* __restrict__ vd, int T, int Hq, int Hk, int L, int lgG,
-    int chunk, int nc_seq, float scale_log2, float* __restrict__ ws_o, float* __restrict__ ws_ml) {
+    const uint16_t* __restrict__ kd, const uint16_t* __restrict__ vd, int T, int Hq, int Hk, int L, int Lcap,
+    int lgG, int chunk, int nc_seq, float scale_log2, float* __restrict__ ws_o, float* __restrict__ ws_ml) {
   using TL = Tile<D>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[4 * kTileBytes<D>];  // two (K, V) tile buffers
   lds_u8* const smem = (lds_u8*)smem_raw;
@@ -93,7 +93,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 4))) void
   uint32_t stride;
   int nkeys;
   if (depth) {
-    const int64_t slab = (static_cast<int64_t>(b) * Hk + hk) * L * D;
+    const int64_t slab = (static_cast<int64_t>(b) * Hk + hk) * Lcap * D;
     kbase = kd + slab;
     vbase = vd + slab;
     stride = D * 2;
@@ -269,7 +269,7 @@ hipError_t launch_decode_d(const DecodeArgs& a) {
                      static_cast<hipStream_t>(a.stream), static_cast<const uint16_t*>(a.q),
                      static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
                      static_cast<const uint16_t*>(a.kd), static_cast<const uint16_t*>(a.vd), a.T, a.Hq, a.Hk, a.L,
-                     lgG, chunk, nc_seq, scale_log2, ws_o, ws_ml);
+                     a.Lcap, lgG, chunk, nc_seq, scale_log2, ws_o, ws_ml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((moda_decode_merge_kernel<D>), dim3(static_cast<unsigned>(a.B * a.Hq)),

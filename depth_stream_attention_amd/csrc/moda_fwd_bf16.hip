@@ -67,7 +67,7 @@ struct Geo {
   __amdgpu_buffer_rsrc_t kd, vd;
   int L;
   uint32_t key_bytes;   // Hk*d*2: stride between consecutive keys of one KV head
-  uint32_t tok_bytes;   // Hk*L*d*2: stride between consecutive tokens' depth slabs
+  uint32_t tok_bytes;   // Hk*Lcap*d*2: stride between consecutive tokens' depth slabs
   int tok_wave;         // tokens per wave (32 / G)
 };
 
@@ -210,7 +210,7 @@ template <int D, bool DEPTH, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void moda_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ kd, const uint16_t* __restrict__ vd, int B, int T, int Hq, int Hk, int L,
-    int lgG, int nrb, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
+    int Lcap, int lgG, int nrb, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
   using TL = Tile<D>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[4 * TL::BYTES];
   lds_u8* const smem = (lds_u8*)smem_raw;
@@ -232,13 +232,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   g.L = DEPTH ? L : 0;
   g.tok_wave = (kRowsPerWave >> lgG) > 0 ? (kRowsPerWave >> lgG) : 1;
   g.key_bytes = static_cast<uint32_t>(Hk) * D * 2;
-  g.tok_bytes = static_cast<uint32_t>(Hk) * (DEPTH ? L : 0) * D * 2;
+  g.tok_bytes = static_cast<uint32_t>(Hk) * (DEPTH ? Lcap : 0) * D * 2;
   const uint16_t* kb = k + (static_cast<int64_t>(b) * T * Hk + hk) * D;
   const uint16_t* vb = v + (static_cast<int64_t>(b) * T * Hk + hk) * D;
   const uint32_t seq_range = (static_cast<uint32_t>(T - 1) * Hk + 1) * D * 2;
   if (DEPTH) {
-    const int64_t slab0 = ((static_cast<int64_t>(b) * T + tb) * Hk + hk) * static_cast<int64_t>(L) * D;
-    const int64_t range = ((static_cast<int64_t>(T - 1 - tb) * Hk + 1) * L) * D * 2;
+    const int64_t slab0 = ((static_cast<int64_t>(b) * T + tb) * Hk + hk) * static_cast<int64_t>(Lcap) * D;
+    const int64_t range = ((static_cast<int64_t>(T - 1 - tb) * Hk + 1) * Lcap) * D * 2;
     const uint32_t dr = static_cast<uint32_t>(range < 0x7fffffff ? range : 0x7fffffff);
     g.kd = make_rsrc(kd + slab0, dr);
     g.vd = make_rsrc(vd + slab0, dr);
@@ -395,7 +395,7 @@ hipError_t launch(const FwdArgs& a) {
                      dim3(kThreads), 0, static_cast<hipStream_t>(a.stream),
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.kd),
-                     static_cast<const uint16_t*>(a.vd), a.B, a.T, a.Hq, a.Hk, a.L, lgG, nrb, scale_log2,
+                     static_cast<const uint16_t*>(a.vd), a.B, a.T, a.Hq, a.Hk, a.L, a.Lcap, lgG, nrb, scale_log2,
                      static_cast<uint16_t*>(a.out), a.lse);
   return hipGetLastError();
 }

@@ -76,8 +76,8 @@ __device__ __forceinline__ void f32_block(F32Row<D>& st, const float* __restrict
 template <int D>
 __global__ __launch_bounds__(kWaves * 64) void moda_fwd_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    const float* __restrict__ kd, const float* __restrict__ vd, int B, int T, int Hq, int Hk, int L, int causal,
-    float scale, float* __restrict__ out, float* __restrict__ lse) {
+    const float* __restrict__ kd, const float* __restrict__ vd, int B, int T, int Hq, int Hk, int L, int Lcap,
+    int causal, float scale, float* __restrict__ out, float* __restrict__ lse) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * kWaves + wave;  // rows in (b, t, h) order
   if (row >= static_cast<int64_t>(B) * T * Hq) return;                  // whole wave leaves together
@@ -109,7 +109,7 @@ __global__ __launch_bounds__(kWaves * 64) void moda_fwd_f32_kernel(
   for (int j0 = 0; j0 < nseq; j0 += 64)
     f32_block<D>(st, kb + j0 * kv_stride, vb + j0 * kv_stride, kv_stride, min(64, nseq - j0), lane, scale);
   if (L > 0) {
-    const int64_t slab = ((static_cast<int64_t>(b) * T + t) * Hk + hk) * L * D;
+    const int64_t slab = ((static_cast<int64_t>(b) * T + t) * Hk + hk) * Lcap * D;
     for (int i0 = 0; i0 < L; i0 += 64)
       f32_block<D>(st, kd + slab + static_cast<int64_t>(i0) * D, vd + slab + static_cast<int64_t>(i0) * D, D,
                    min(64, L - i0), lane, scale);
@@ -129,7 +129,7 @@ hipError_t launch_d(const FwdArgs& a) {
   hipLaunchKernelGGL((moda_fwd_f32_kernel<D>), dim3(blocks), dim3(kWaves * 64), 0,
                      static_cast<hipStream_t>(a.stream), static_cast<const float*>(a.q),
                      static_cast<const float*>(a.k), static_cast<const float*>(a.v),
-                     static_cast<const float*>(a.kd), static_cast<const float*>(a.vd), a.B, a.T, a.Hq, a.Hk, a.L,
+                     static_cast<const float*>(a.kd), static_cast<const float*>(a.vd), a.B, a.T, a.Hq, a.Hk, a.L, a.Lcap,
                      a.causal, 1.0f / sqrtf(static_cast<float>(D)), static_cast<float*>(a.out), a.lse);
   return hipGetLastError();
 }

@@ -9,6 +9,7 @@ namespace moda {
 struct FwdArgs {
   const void *q, *k, *v, *kd, *vd;
   int B, T, Hq, Hk, d, L, causal;
+  int Lcap;  // depth slots per (token, KV head) in memory; the first L are attended
   void* out;
   float* lse;
   void* stream;
@@ -17,6 +18,7 @@ struct FwdArgs {
 struct DecodeArgs {
   const void *q, *k, *v, *kd, *vd;  // q [B][Hq][d]; caches [B][T][Hk][d]; depth [B][Hk][L][d]
   int B, T, Hq, Hk, d, L;
+  int Lcap;    // depth slots per (batch, KV head) in memory; the first L are attended
   void* out;   // [B][Hq][d]
   float* lse;  // [B][Hq]
   void* workspace;

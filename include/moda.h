@@ -82,6 +82,22 @@ int moda_attn_fwd(const void* q, const void* k_seq, const void* v_seq, const voi
                   void* out, float* lse, moda_stream_t stream);
 
 /*
+ * moda_attn_fwd over a bounded depth cache ([Summ] 6.2 future work: a sliding
+ * window of the most recent S layers in place of all of them).  The packed
+ * depth stream holds S slots per (token, KV head) -- k_depth, v_depth are
+ * [B][T][Hk][S][d] -- filled as a ring (layer l writes slot l mod S with
+ * moda_append_depth_slot), and the first L <= S slots are attended: L = S once
+ * the ring is full, L = the number of layers written before that.  The softmax
+ * does not depend on the order of the depth slots, so ring order needs no
+ * unrolling.  Slots L..S-1 are never read.  Other arguments, layouts and errors
+ * as moda_attn_fwd, plus MODA_ERR_SHAPE when S < L; the 2^31 limit applies to
+ * 129*Hk*S*d*2 bytes.  moda_attn_fwd(..., L, ...) equals this call with S = L.
+ */
+int moda_attn_fwd_ring(const void* q, const void* k_seq, const void* v_seq, const void* k_depth,
+                       const void* v_depth, int B, int T, int Hq, int Hk, int d, int S, int L, int causal,
+                       void* out, float* lse, moda_stream_t stream);
+
+/*
  * The same operation with fp32 inputs and fp32 output, computed in fp32.
  * Arguments, layouts and errors are those of moda_attn_fwd with every bf16
  * tensor replaced by an fp32 one (without the bf16 byte-offset limits).
@@ -132,6 +148,16 @@ int moda_attn_fwd_f32(const void* q, const void* k_seq, const void* v_seq, const
 int moda_attn_decode(const void* q, const void* k_cache, const void* v_cache, const void* k_depth,
                      const void* v_depth, int B, int T, int Hq, int Hk, int d, int L, void* out, float* lse,
                      void* workspace, size_t workspace_bytes, moda_stream_t stream);
+
+/*
+ * moda_attn_decode over a bounded depth cache: k_depth, v_depth are
+ * [B][Hk][S][d] ring slots of which the first L <= S are attended (see
+ * moda_attn_fwd_ring).  Workspace as for moda_attn_decode with this L.
+ * MODA_ERR_SHAPE when S < L.
+ */
+int moda_attn_decode_ring(const void* q, const void* k_cache, const void* v_cache, const void* k_depth,
+                          const void* v_depth, int B, int T, int Hq, int Hk, int d, int S, int L, void* out,
+                          float* lse, void* workspace, size_t workspace_bytes, moda_stream_t stream);
 
 /*
  * Workspace bytes moda_attn_decode needs for these sizes (host only; 0 when a

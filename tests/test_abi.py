@@ -129,3 +129,18 @@ def test_decode_validation(lib):
         assert decode(lib, **kw) == api.MODA_ERR_UNSUPPORTED, kw
     for kw in (dict(q=MIS), dict(kc=MIS), dict(vc=MIS), dict(kd=MIS), dict(vd=MIS), dict(out=MIS), dict(ws=MIS)):
         assert decode(lib, **kw) == api.MODA_ERR_ALIGN, kw
+
+
+def test_ring_validation(lib):
+    null = ctypes.c_void_p(0)
+    ring = lambda S, L, kd=A, vd=A: lib.moda_attn_fwd_ring(A, A, A, kd, vd, 1, 16, 4, 2, 128, S, L, 1, A2, A2,
+                                                             None)
+    assert ring(4, 5) == api.MODA_ERR_SHAPE            # more attended slots than the ring holds
+    assert ring(4, -1) == api.MODA_ERR_SHAPE
+    assert ring(4, 2, kd=null) == api.MODA_ERR_NULL
+    assert ring(4, 2, vd=MIS) == api.MODA_ERR_ALIGN
+    assert ring(1 << 20, 2) == api.MODA_ERR_UNSUPPORTED  # slot stride beyond the 32-bit offsets
+    dec = lambda S, L: lib.moda_attn_decode_ring(A, A, A, A, A, 1, 300, 8, 2, 128, S, L, A2, A2, A2,
+                                                 lib.moda_attn_decode_workspace(1, 300, 8, 2, 128, max(L, 0)), None)
+    assert dec(4, 5) == api.MODA_ERR_SHAPE
+    assert dec(4, -1) == api.MODA_ERR_SHAPE
