@@ -7,6 +7,7 @@ imports it.
 from .oracle import (  # noqa: F401
     moda_fwd,
     moda_fwd_rows,
+    moda_bwd,
     pack_depth,
     append_depth_slot,
     default_threads,

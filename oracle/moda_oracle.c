@@ -1,6 +1,6 @@
 /*
  * moda_oracle.c -- plain fp64 CPU oracle for the Mixture-of-Depths Attention
- * (MoDA) forward and for the depth-stream packing permutation.
+ * (MoDA) forward, its gradients, and the depth-stream packing permutation.
  *
  * TEST INFRASTRUCTURE ONLY.  This file is the correctness reference that the
  * HIP path is checked against.  Only the tests, the smoke check and the
@@ -252,6 +252,147 @@ int moda_oracle_fwd(const void* q, const void* k_seq, const void* v_seq, const v
   free(rows);
   free(lse_rows);
   return rc;
+}
+
+/* ---- backward ------------------------------------------------------------ */
+
+/* Gradients of the forward map, by definition: with P_n the softmax weights of
+ * row (b, t, h) over its candidates n (the visible sequence keys j, then the L
+ * depth slots i), dO the output gradient of the row and
+ *   dP_n = <dO, v_n>,   D = sum_n P_n dP_n,   dS_n = P_n (dP_n - D)
+ * (the derivative of out = sum_n P_n v_n through the shared denominator):
+ *   dq      = s * sum_n dS_n k_n
+ *   dk_n   += s * dS_n q          (summed over every row that sees key n)
+ *   dv_n   += P_n dO
+ * Sequence keys collect contributions from the G heads of every token that
+ * sees them; a depth slot of token t only from the G heads of token t.
+ * One thread owns one (b, hk): all of that head's keys and the G query heads
+ * that read them, so its sums need no synchronisation. */
+typedef struct {
+  const orc_problem* p;
+  const void* dout;
+  int first, last; /* (b, hk) pairs [first, last) */
+  double *dq, *dk, *dv, *dkd, *dvd;
+} orc_bwd_job;
+
+static void* orc_bwd_worker(void* arg) {
+  orc_bwd_job* job = (orc_bwd_job*)arg;
+  const orc_problem* p = job->p;
+  const int G = p->Hq / p->Hk, d = p->d, T = p->T, L = p->L;
+  const double s = 1.0 / sqrt((double)p->d);
+  double* w = (double*)malloc(sizeof(double) * ((size_t)3 * (T + L) + 2 * (size_t)d));
+  if (!w) return (void*)1;
+  double* logit = w;            /* [T + L]: logits, then P */
+  double* dP = w + (T + L);     /* [T + L] */
+  double* dS = w + 2 * (T + L); /* [T + L] */
+  double* qrow = w + 3 * (T + L);
+  double* dorow = qrow + d;
+  for (int pair = job->first; pair < job->last; ++pair) {
+    const int b = pair / p->Hk, hk = pair % p->Hk;
+    for (int t = 0; t < T; ++t)
+      for (int g = 0; g < G; ++g) {
+        const int h = hk * G + g;
+        const int nseq = p->causal ? t + 1 : T;
+        const int ncand = nseq + L;
+        for (int c = 0; c < d; ++c) {
+          qrow[c] = orc_load(p->q, ix_q(p, b, t, h, c), p->kind);
+          dorow[c] = orc_load(job->dout, ix_q(p, b, t, h, c), p->kind);
+        }
+        /* Forward recomputation: logits, the row max, P. */
+        double m = -INFINITY;
+        for (int n = 0; n < ncand; ++n) {
+          double dot = 0.0, dpv = 0.0;
+          for (int c = 0; c < d; ++c) {
+            const size_t kix = n < nseq ? ix_kv(p, b, n, hk, c) : ix_depth(p, b, t, n - nseq, hk, c);
+            const double kc = orc_load(n < nseq ? p->k_seq : p->k_depth, kix, p->kind);
+            const double vc = orc_load(n < nseq ? p->v_seq : p->v_depth, kix, p->kind);
+            dot += qrow[c] * kc;
+            dpv += dorow[c] * vc;
+          }
+          logit[n] = s * dot;
+          dP[n] = dpv;
+          if (logit[n] > m) m = logit[n];
+        }
+        double Z = 0.0;
+        for (int n = 0; n < ncand; ++n) {
+          const double e = exp(logit[n] - m);
+          logit[n] = e;
+          Z += e;
+        }
+        double D = 0.0;
+        for (int n = 0; n < ncand; ++n) {
+          logit[n] /= Z; /* P_n */
+          D += logit[n] * dP[n];
+        }
+        for (int n = 0; n < ncand; ++n) dS[n] = logit[n] * (dP[n] - D);
+        /* Accumulate. */
+        for (int c = 0; c < d; ++c) {
+          double acc = 0.0;
+          for (int n = 0; n < ncand; ++n) {
+            const size_t kix = n < nseq ? ix_kv(p, b, n, hk, c) : ix_depth(p, b, t, n - nseq, hk, c);
+            acc += dS[n] * orc_load(n < nseq ? p->k_seq : p->k_depth, kix, p->kind);
+            double* dkp = n < nseq ? job->dk : job->dkd;
+            double* dvp = n < nseq ? job->dv : job->dvd;
+            dkp[kix] += s * dS[n] * qrow[c];
+            dvp[kix] += logit[n] * dorow[c];
+          }
+          job->dq[ix_q(p, b, t, h, c)] = s * acc;
+        }
+      }
+  }
+  free(w);
+  return NULL;
+}
+
+/* Gradients of every input for the output gradient dout ([B][T][Hq][d], same
+ * kind as the inputs).  Outputs fp64, in the input layouts: dq [B][T][Hq][d];
+ * dk, dv [B][T][Hk][d]; dkd, dvd [B][T][L][Hk][d].  Returns 0 or a negative code. */
+int moda_oracle_bwd(const void* q, const void* k_seq, const void* v_seq, const void* k_depth,
+                    const void* v_depth, const void* dout, int kind, int B, int T, int Hq, int Hk, int d,
+                    int L, int causal, double* dq, double* dk, double* dv, double* dkd, double* dvd,
+                    int nthreads) {
+  orc_problem p = {q, k_seq, v_seq, k_depth, v_depth, kind, B, T, Hq, Hk, d, L, causal};
+  int rc = orc_check(&p);
+  if (rc) return rc;
+  if (!dout || !dq || !dk || !dv || (L > 0 && (!dkd || !dvd))) return -1;
+  memset(dq, 0, sizeof(double) * (size_t)B * T * Hq * d);
+  memset(dk, 0, sizeof(double) * (size_t)B * T * Hk * d);
+  memset(dv, 0, sizeof(double) * (size_t)B * T * Hk * d);
+  if (L > 0) {
+    memset(dkd, 0, sizeof(double) * (size_t)B * T * L * Hk * d);
+    memset(dvd, 0, sizeof(double) * (size_t)B * T * L * Hk * d);
+  }
+  const int npairs = B * Hk;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > npairs) nthreads = npairs;
+  pthread_t* tid = (pthread_t*)malloc(sizeof(pthread_t) * nthreads);
+  orc_bwd_job* jobs = (orc_bwd_job*)malloc(sizeof(orc_bwd_job) * nthreads);
+  if (!tid || !jobs) {
+    free(tid);
+    free(jobs);
+    return -5;
+  }
+  for (int w = 0; w < nthreads; ++w) {
+    orc_bwd_job j = {&p, dout, npairs * w / nthreads, npairs * (w + 1) / nthreads, dq, dk, dv, dkd, dvd};
+    jobs[w] = j;
+  }
+  int failed = 0;
+  for (int w = 1; w < nthreads; ++w)
+    if (pthread_create(&tid[w], NULL, orc_bwd_worker, &jobs[w]) != 0) {
+      tid[w] = 0;
+      if (orc_bwd_worker(&jobs[w]) != NULL) failed = 1;
+    }
+  if (orc_bwd_worker(&jobs[0]) != NULL) failed = 1;
+  for (int w = 1; w < nthreads; ++w) {
+    void* res = NULL;
+    if (tid[w]) {
+      pthread_join(tid[w], &res);
+      if (res != NULL) failed = 1;
+    }
+  }
+  free(tid);
+  free(jobs);
+  return failed ? -5 : 0;
 }
 
 /* Depth-stream packing, by definition: dst[b][t][hk][l][:] = src[b][t][l][hk][:]

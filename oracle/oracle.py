@@ -32,6 +32,8 @@ def _load():
         lib.moda_oracle_fwd.restype = i32
         lib.moda_oracle_fwd_rows.argtypes = [vp] * 5 + [i32] * 8 + [vp, i64, vp, vp, i32]
         lib.moda_oracle_fwd_rows.restype = i32
+        lib.moda_oracle_bwd.argtypes = [vp] * 6 + [i32] * 8 + [vp] * 5 + [i32]
+        lib.moda_oracle_bwd.restype = i32
         lib.moda_oracle_pack_depth.argtypes = [vp, vp] + [i32] * 6
         lib.moda_oracle_pack_depth.restype = i32
         lib.moda_oracle_append_depth_slot.argtypes = [vp, vp] + [i32] * 7
@@ -125,6 +127,31 @@ def moda_fwd_rows(q, k_seq, v_seq, k_depth, v_depth, rows, causal=True, nthreads
     if rc != 0:
         raise RuntimeError("moda_oracle_fwd_rows failed with code %d" % rc)
     return out, lse
+
+
+def moda_bwd(q, k_seq, v_seq, k_depth, v_depth, dout, causal=True, nthreads=None):
+    """Gradients of every input for the output gradient dout [B,T,Hq,d], in fp64.
+
+    Returns (dq [B,T,Hq,d], dk, dv [B,T,Hk,d], dkd, dvd [B,T,L,Hk,d]); the depth
+    gradients are None when L == 0.  dout must share the inputs' dtype.
+    """
+    lib = _load()
+    (qa, ka, va, kda, vda), kind, (B, T, Hq, Hk, d, L) = _prepare(q, k_seq, v_seq, k_depth, v_depth)
+    da, dkind = _host(dout)
+    if dkind != kind or da.shape != qa.shape:
+        raise ValueError("dout must be [B,T,Hq,d] with the inputs' dtype")
+    dq = np.empty((B, T, Hq, d), np.float64)
+    dk = np.empty((B, T, Hk, d), np.float64)
+    dv = np.empty((B, T, Hk, d), np.float64)
+    dkd = np.empty((B, T, L, Hk, d), np.float64) if L else None
+    dvd = np.empty((B, T, L, Hk, d), np.float64) if L else None
+    rc = lib.moda_oracle_bwd(_ptr(qa), _ptr(ka), _ptr(va), _ptr(kda), _ptr(vda), _ptr(da), kind,
+                             B, T, Hq, Hk, d, L, int(bool(causal)),
+                             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dkd), _ptr(dvd),
+                             nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError("moda_oracle_bwd failed with code %d" % rc)
+    return dq, dk, dv, dkd, dvd
 
 
 def _raw_bytes(x):

@@ -203,3 +203,119 @@ def pin_depth_aligned(seed):
     out, _ = oracle.moda_fwd(q, k, v, kd.contiguous(), vd, nthreads=2)
     mass = out[0, :, 0, 0]                                    # head 0, depth mass per position
     assert mass.min() > 0.9, "depth mass of the aligned head fell to %g" % mass.min()
+
+
+# ---- gradients ----------------------------------------------------------------
+
+def autograd_reference(q, k, v, kd, vd, dout, causal):
+    """Gradients of sum(dout * MoDA(q, k, v, kd, vd)) by torch autograd in fp64.
+
+    The forward is written with plain tensor ops on the explicitly concatenated
+    [sequence | depth] key set of every row (head h reads KV head h // G), so
+    the derivative comes from torch's own autograd, not from a hand-written rule.
+    Returns numpy (dq, dk, dv, dkd, dvd) in the input layouts.
+    """
+    leaves = [x.detach().clone().requires_grad_(True) for x in (q, k, v, kd, vd)]
+    q_, k_, v_, kd_, vd_ = leaves
+    B, T, Hq, d = q.shape
+    Hk = k.shape[2]
+    G = Hq // Hk
+    L = kd.shape[2]
+    ke = k_.repeat_interleave(G, dim=2).permute(0, 2, 1, 3)           # [B,Hq,T,d]
+    ve = v_.repeat_interleave(G, dim=2).permute(0, 2, 1, 3)
+    kde = kd_.repeat_interleave(G, dim=3).permute(0, 3, 1, 2, 4)      # [B,Hq,T,L,d]
+    vde = vd_.repeat_interleave(G, dim=3).permute(0, 3, 1, 2, 4)
+    kall = torch.cat([ke.unsqueeze(2).expand(B, Hq, T, T, d), kde], dim=3)
+    vall = torch.cat([ve.unsqueeze(2).expand(B, Hq, T, T, d), vde], dim=3)
+    mask = torch.ones(T, T + L, dtype=torch.bool)
+    if causal:
+        mask[:, :T] = torch.ones(T, T, dtype=torch.bool).tril()
+    qq = q_.permute(0, 2, 1, 3).unsqueeze(3)                           # [B,Hq,T,1,d]
+    logits = torch.matmul(qq, kall.transpose(-1, -2).contiguous()) / math.sqrt(d)
+    logits = logits.masked_fill(~mask.view(1, 1, T, 1, T + L), float("-inf"))
+    out = torch.matmul(torch.softmax(logits, dim=-1), vall).squeeze(3).permute(0, 2, 1, 3)
+    (out * dout).sum().backward()
+    return tuple(x.grad.numpy() for x in leaves)
+
+
+def pin_bwd_autograd(B, T, Hq, Hk, d, L, causal, seed, tol=1e-11):
+    q, k, v, kd, vd = rand_problem(B, T, Hq, Hk, d, L, seed)
+    dout = torch.randn(B, T, Hq, d, generator=torch.Generator("cpu").manual_seed(seed + 7), dtype=torch.float64)
+    got = oracle.moda_bwd(q, k, v, kd, vd, dout, causal=causal, nthreads=2)
+    want = autograd_reference(q, k, v, kd, vd, dout, causal)
+    for name, g, w in zip(("dq", "dk", "dv", "dkd", "dvd"), got, want):
+        if g is None:
+            assert L == 0 and w.size == 0
+            continue
+        err = np.abs(g - w).max()
+        assert err <= tol * max(1.0, np.abs(w).max()), "%s differs from torch autograd by %g" % (name, err)
+
+
+def pin_bwd_l0_gqa(B, T, Hq, Hk, d, causal, seed, tol=1e-11):
+    """L=0: gradients equal those of torch's GQA SDPA (heads expanded by repeat_interleave)."""
+    q, k, v, _, _ = rand_problem(B, T, Hq, Hk, d, 0, seed)
+    dout = torch.randn(B, T, Hq, d, generator=torch.Generator("cpu").manual_seed(seed + 3), dtype=torch.float64)
+    dq, dk, dv, dkd, dvd = oracle.moda_bwd(q, k, v, None, None, dout, causal=causal, nthreads=2)
+    assert dkd is None and dvd is None
+    G = Hq // Hk
+    leaves = [x.clone().requires_grad_(True) for x in (q, k, v)]
+    ref = F.scaled_dot_product_attention(
+        leaves[0].permute(0, 2, 1, 3), leaves[1].repeat_interleave(G, dim=2).permute(0, 2, 1, 3),
+        leaves[2].repeat_interleave(G, dim=2).permute(0, 2, 1, 3), is_causal=bool(causal))
+    (ref.permute(0, 2, 1, 3) * dout).sum().backward()
+    for name, g, leaf in zip(("dq", "dk", "dv"), (dq, dk, dv), leaves):
+        err = np.abs(g - leaf.grad.numpy()).max()
+        assert err <= tol, "L=0 %s differs from GQA SDPA autograd by %g" % (name, err)
+
+
+def pin_bwd_finite_difference(seed, h=1e-5):
+    """Directional derivatives of F = sum(dout * out) by central differences of the
+    fp64 forward oracle must equal <grad, delta> for a random direction per input."""
+    B, T, Hq, Hk, d, L = 1, 7, 4, 2, 8, 3
+    xs = list(rand_problem(B, T, Hq, Hk, d, L, seed))
+    g = torch.Generator("cpu").manual_seed(seed + 11)
+    dout = torch.randn(B, T, Hq, d, generator=g, dtype=torch.float64)
+    grads = oracle.moda_bwd(*xs, dout, nthreads=1)
+
+    def F_of(args):
+        out, _ = oracle.moda_fwd(*args, nthreads=1)
+        return float((out * dout.numpy()).sum())
+
+    for i, name in enumerate(("q", "k_seq", "v_seq", "k_depth", "v_depth")):
+        delta = torch.randn(xs[i].shape, generator=g, dtype=torch.float64)
+        plus = list(xs)
+        minus = list(xs)
+        plus[i] = xs[i] + h * delta
+        minus[i] = xs[i] - h * delta
+        fd = (F_of(plus) - F_of(minus)) / (2 * h)
+        an = float((grads[i] * delta.numpy()).sum())
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), \
+            "d/d%s: finite difference %.12g vs gradient %.12g" % (name, fd, an)
+
+
+def pin_bwd_invariants(seed):
+    """Softmax weights sum to one in every row, so per (b, KV head):
+    sum of all value gradients (sequence + depth) = sum of dout over the group's rows, and
+    sum of all key gradients = 0.  Equal values everywhere make out constant, so then every
+    query and key gradient vanishes and the value gradients stay those of the weights."""
+    B, T, Hq, Hk, d, L = 2, 12, 6, 2, 8, 4
+    q, k, v, kd, vd = rand_problem(B, T, Hq, Hk, d, L, seed)
+    dout = torch.randn(B, T, Hq, d, generator=torch.Generator("cpu").manual_seed(seed + 5), dtype=torch.float64)
+    dq, dk, dv, dkd, dvd = oracle.moda_bwd(q, k, v, kd, vd, dout, nthreads=2)
+    G = Hq // Hk
+    for b in range(B):
+        for hk in range(Hk):
+            sv = dv[b, :, hk].sum(0) + dvd[b, :, :, hk].sum((0, 1))
+            want = dout[b, :, hk * G:(hk + 1) * G].sum((0, 1)).numpy()
+            assert np.abs(sv - want).max() <= 1e-11, "value-gradient mass not conserved"
+            sk = dk[b, :, hk].sum(0) + dkd[b, :, :, hk].sum((0, 1))
+            assert np.abs(sk).max() <= 1e-11, "key gradients must sum to zero"
+    vc = torch.full_like(v, 0.5)
+    vdc = torch.full_like(vd, 0.5)
+    dq2, dk2, dv2, dkd2, dvd2 = oracle.moda_bwd(q, k, vc, kd, vdc, dout, nthreads=2)
+    assert np.abs(dq2).max() <= 1e-13 and np.abs(dk2).max() <= 1e-13 and np.abs(dkd2).max() <= 1e-13
+    # value gradients do not depend on the values
+    assert np.abs(dv2 - dv).max() <= 1e-13 and np.abs(dvd2 - dvd).max() <= 1e-13
+    # zero output gradient -> every gradient zero
+    z = oracle.moda_bwd(q, k, v, kd, vd, torch.zeros_like(dout), nthreads=2)
+    assert all(np.abs(x).max() == 0.0 for x in z)

@@ -6,6 +6,7 @@ import pytest
 import torch
 
 import oracle
+import oracle_pins as pins
 from oracle_pins import (pin_convex_and_permutation, pin_depth_aligned, pin_head_expansion,
                          pin_l0_is_gqa, pin_merge_identity, pin_sdpa, pin_t1_closed_form,
                          pin_t1_depth, pin_worked_example, rand_problem)
@@ -126,3 +127,37 @@ def test_append_depth_slot_matches_slice_assignment():
     assert np.array_equal(got, want)
     with pytest.raises(RuntimeError):
         oracle.append_depth_slot(kv, dst, 5)
+
+
+# ---- gradients ----------------------------------------------------------------
+
+@pytest.mark.parametrize("causal,G,Hk,L", [(True, 2, 2, 3), (False, 1, 2, 2), (True, 4, 1, 0), (True, 1, 1, 6)])
+def test_bwd_matches_torch_autograd(causal, G, Hk, L):
+    pins.pin_bwd_autograd(2, 11, G * Hk, Hk, 8, L, causal, 300 + 7 * G + L)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_bwd_l0_matches_gqa_sdpa_autograd(causal):
+    pins.pin_bwd_l0_gqa(2, 17, 4, 2, 16, causal, 310)
+
+
+def test_bwd_finite_differences():
+    pins.pin_bwd_finite_difference(320)
+
+
+def test_bwd_invariants():
+    pins.pin_bwd_invariants(330)
+
+
+def test_bwd_thread_count_and_bf16_widening():
+    q, k, v, kd, vd = pins.rand_problem(2, 10, 4, 2, 8, 3, 340)
+    dout = torch.randn(2, 10, 4, 8, generator=torch.Generator("cpu").manual_seed(341), dtype=torch.float64)
+    a = oracle.moda_bwd(q, k, v, kd, vd, dout, nthreads=1)
+    b = oracle.moda_bwd(q, k, v, kd, vd, dout, nthreads=4)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    bf = [x.to(torch.bfloat16) for x in (q, k, v, kd, vd, dout)]
+    c = oracle.moda_bwd(*bf, nthreads=2)
+    d = oracle.moda_bwd(*[x.double() for x in bf], nthreads=2)
+    for x, y in zip(c, d):
+        assert np.array_equal(x, y)

@@ -33,6 +33,14 @@ MUTANTS = {
         "acc += logit[nseq + i] * orc_load(p->v_depth, ix_depth(p, b, t, i, hk, c), p->kind);",
         "acc += logit[nseq + i] * orc_load(p->k_depth, ix_depth(p, b, t, i, hk, c), p->kind);"),
     "depth_logits_unscaled": ("    logit[nseq + i] = s * dot;", "    logit[nseq + i] = dot;"),
+    # gradients
+    "bwd_drops_row_correction": ("dS[n] = logit[n] * (dP[n] - D);", "dS[n] = logit[n] * dP[n];"),
+    "bwd_dk_unscaled": ("dkp[kix] += s * dS[n] * qrow[c];", "dkp[kix] += dS[n] * qrow[c];"),
+    "bwd_dv_weighted_by_dP": ("dvp[kix] += logit[n] * dorow[c];", "dvp[kix] += dP[n] * dorow[c];"),
+    "bwd_dq_sign": ("job->dq[ix_q(p, b, t, h, c)] = s * acc;", "job->dq[ix_q(p, b, t, h, c)] = -s * acc;"),
+    "bwd_causal_sees_all": ("const int nseq = p->causal ? t + 1 : T;", "const int nseq = T;"),
+    "bwd_interleaved_head_map": ("const int h = hk * G + g;", "const int h = g * p->Hk + hk;"),
+    "bwd_unnormalised_weights": ("logit[n] /= Z; /* P_n */", "logit[n] /= Z * Z; /* P_n */"),
 }
 
 ALL_PINS = [
@@ -46,6 +54,10 @@ ALL_PINS = [
     lambda: pins.pin_convex_and_permutation(107),
     lambda: pins.pin_merge_identity(108),
     lambda: pins.pin_depth_aligned(109),
+    lambda: pins.pin_bwd_autograd(2, 9, 4, 2, 8, 3, True, 110),
+    lambda: pins.pin_bwd_l0_gqa(1, 11, 4, 2, 8, True, 111),
+    lambda: pins.pin_bwd_finite_difference(112),
+    lambda: pins.pin_bwd_invariants(113),
 ]
 
 
@@ -65,7 +77,7 @@ def _build_mutant(tmp_path, name):
 def test_pins_reject_planted_mistake(tmp_path, monkeypatch, name):
     good = orc._load()
     mutant = ctypes.CDLL(_build_mutant(tmp_path, name))
-    for fn in ("moda_oracle_fwd", "moda_oracle_fwd_rows", "moda_oracle_pack_depth",
+    for fn in ("moda_oracle_fwd", "moda_oracle_fwd_rows", "moda_oracle_bwd", "moda_oracle_pack_depth",
                "moda_oracle_append_depth_slot"):
         getattr(mutant, fn).argtypes = getattr(good, fn).argtypes
         getattr(mutant, fn).restype = getattr(good, fn).restype
