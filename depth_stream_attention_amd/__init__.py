@@ -6,6 +6,8 @@ include/moda.h); this package is its thin Python binding.
 from .api import (  # noqa: F401
     MODAError,
     moda_append_depth_slot,
+    moda_attn_bwd,
+    moda_attn_bwd_workspace,
     moda_attn_fwd,
     moda_attn_fwd_f32,
     moda_block_span,

@@ -110,6 +110,65 @@ def moda_attn_fwd_f32(q, k_seq, v_seq, k_depth=None, v_depth=None, causal=True, 
     return _fwd("moda_attn_fwd_f32", torch.float32, q, k_seq, v_seq, k_depth, v_depth, causal, out, lse, stream)
 
 
+def moda_attn_bwd_workspace(B, T, Hq, Hk, d, L):
+    """Bytes of workspace moda_attn_bwd needs (0 for invalid sizes)."""
+    return int(_lib.load().moda_attn_bwd_workspace(B, T, Hq, Hk, d, L))
+
+
+def moda_attn_bwd(q, k_seq, v_seq, k_depth, v_depth, out, lse, dout, causal=True, grads=None, workspace=None,
+                  stream=None):
+    """MoDA backward, bf16.  Inputs as given to moda_attn_fwd (k_depth, v_depth packed [B,T,Hk,L,d] or None),
+    that call's (out, lse), and dout [B,T,Hq,d].  grads: optional preallocated (dq, dk, dv, dkd, dvd);
+    workspace: a uint8 GPU tensor of at least moda_attn_bwd_workspace(...) bytes (allocated here when None).
+    Returns (dq [B,T,Hq,d], dk_seq, dv_seq [B,T,Hk,d], dk_depth, dv_depth [B,T,Hk,L,d] or None), all bf16."""
+    dtype = torch.bfloat16
+    for t, n in ((q, "q"), (k_seq, "k_seq"), (v_seq, "v_seq"), (out, "out"), (dout, "dout")):
+        _check(t, n, dtype, 4)
+    _check(lse, "lse", torch.float32, 3)
+    B, T, Hq, d = q.shape
+    Hk = k_seq.shape[2]
+    if tuple(k_seq.shape) != (B, T, Hk, d) or tuple(v_seq.shape) != (B, T, Hk, d):
+        raise ValueError("k_seq / v_seq must be [B,T,Hk,d] = %s" % ((B, T, Hk, d),))
+    if tuple(out.shape) != (B, T, Hq, d) or tuple(dout.shape) != (B, T, Hq, d) or tuple(lse.shape) != (B, Hq, T):
+        raise ValueError("out, dout must be [B,T,Hq,d] and lse [B,Hq,T]")
+    L = 0
+    if k_depth is not None and k_depth.numel() > 0:
+        _check(k_depth, "k_depth", dtype, 5)
+        _check(v_depth, "v_depth", dtype, 5)
+        L = k_depth.shape[3]
+        if tuple(k_depth.shape) != (B, T, Hk, L, d) or tuple(v_depth.shape) != (B, T, Hk, L, d):
+            raise ValueError("packed depth K/V must be [B,T,Hk,L,d] = %s" % ((B, T, Hk, L, d),))
+    else:
+        k_depth = v_depth = None
+    if grads is None:
+        dev = q.device
+        grads = (torch.empty_like(q), torch.empty_like(k_seq), torch.empty_like(v_seq),
+                 torch.empty((B, T, Hk, L, d), dtype=dtype, device=dev) if L else None,
+                 torch.empty((B, T, Hk, L, d), dtype=dtype, device=dev) if L else None)
+    dq, dk, dv, dkd, dvd = grads
+    _check(dq, "dq", dtype, 4)
+    _check(dk, "dk_seq", dtype, 4)
+    _check(dv, "dv_seq", dtype, 4)
+    if tuple(dq.shape) != (B, T, Hq, d) or tuple(dk.shape) != (B, T, Hk, d) or tuple(dv.shape) != (B, T, Hk, d):
+        raise ValueError("dq must be [B,T,Hq,d] and dk_seq, dv_seq [B,T,Hk,d]")
+    if L:
+        _check(dkd, "dk_depth", dtype, 5)
+        _check(dvd, "dv_depth", dtype, 5)
+        if tuple(dkd.shape) != (B, T, Hk, L, d) or tuple(dvd.shape) != (B, T, Hk, L, d):
+            raise ValueError("dk_depth / dv_depth must be [B,T,Hk,L,d]")
+    need = moda_attn_bwd_workspace(B, T, Hq, Hk, d, L)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check(workspace, "workspace", torch.uint8, 1)
+    rc = _lib.load().moda_attn_bwd(_ptr(q), _ptr(k_seq), _ptr(v_seq), _ptr(k_depth), _ptr(v_depth), _ptr(out),
+                                   _ptr(lse), _ptr(dout), B, T, Hq, Hk, d, L, int(bool(causal)),
+                                   _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dkd if L else None), _ptr(dvd if L else None),
+                                   _ptr(workspace), workspace.numel(), _stream(stream))
+    if rc != MODA_OK:
+        raise MODAError("moda_attn_bwd", rc)
+    return dq, dk, dv, (dkd if L else None), (dvd if L else None)
+
+
 def moda_attn_decode_workspace(B, T, Hq, Hk, d, L):
     """Bytes of workspace moda_attn_decode needs (0 for invalid sizes)."""
     return int(_lib.load().moda_attn_decode_workspace(B, T, Hq, Hk, d, L))

@@ -10,12 +10,14 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoda.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["moda_api.cpp", "moda_fwd_bf16.hip", "moda_fwd_f32.hip", "moda_pack.hip", "moda_decode.hip"]
+SOURCES = ["moda_api.cpp", "moda_fwd_bf16.hip", "moda_fwd_f32.hip", "moda_pack.hip", "moda_decode.hip",
+           "moda_bwd.hip"]
 
 # Per-source extra flags.  The bf16 kernels never produce NaN from finite
 # inputs, and without NaN semantics each fmaxf in their row-max chains needs no
 # canonicalising v_max_f32 x, x before the v_max3_f32.
-SOURCE_FLAGS = {"moda_fwd_bf16.hip": ["-fno-honor-nans"], "moda_decode.hip": ["-fno-honor-nans"]}
+SOURCE_FLAGS = {"moda_fwd_bf16.hip": ["-fno-honor-nans"], "moda_decode.hip": ["-fno-honor-nans"],
+                "moda_bwd.hip": ["-fno-honor-nans"]}
 
 # Packed-fp32 VALU forms are switched off for all device code.
 HIPCC_FLAGS = [

@@ -64,6 +64,31 @@ int validate_decode(const void* q, const void* k, const void* v, const void* kd,
   return MODA_OK;
 }
 
+int validate_bwd(const void* q, const void* k, const void* v, const void* kd, const void* vd, const void* out,
+                 const float* lse, const void* dout, int B, int T, int Hq, int Hk, int d, int L, int causal,
+                 const void* dq, const void* dk, const void* dv, const void* dkd, const void* dvd, const void* ws,
+                 size_t ws_bytes) {
+  if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv || !ws) return MODA_ERR_NULL;
+  if (L > 0 && (!kd || !vd || !dkd || !dvd)) return MODA_ERR_NULL;
+  if (B <= 0 || T <= 0 || Hq <= 0 || Hk <= 0 || d <= 0 || L < 0) return MODA_ERR_SHAPE;
+  if (Hq % Hk != 0) return MODA_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return MODA_ERR_SHAPE;
+  if (d != 64 && d != 128) return MODA_ERR_UNSUPPORTED;
+  if (!is_pow2_in(Hq / Hk, 1, 16)) return MODA_ERR_UNSUPPORTED;
+  // One (batch) sequence of q or dO, and of one KV head's keys, is addressed
+  // with 32-bit byte offsets; grids and expanded rows stay in int32.
+  if (static_cast<int64_t>(T + 128) * Hq * d * 2 >= (int64_t{1} << 31)) return MODA_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(T) * (Hq / Hk) > INT_MAX / 2) return MODA_ERR_UNSUPPORTED;
+  if (moda::bwd_grid_blocks(B, T, Hq, Hk) > INT_MAX) return MODA_ERR_UNSUPPORTED;
+  if (ws_bytes < moda::bwd_workspace_bytes(B, T, Hq, d, L)) return MODA_ERR_SHAPE;
+  for (const void* p : {q, k, v, out, static_cast<const void*>(lse), dout, dq, dk, dv, ws})
+    if (!aligned16(p)) return MODA_ERR_ALIGN;
+  if (L > 0)
+    for (const void* p : {kd, vd, dkd, dvd})
+      if (!aligned16(p)) return MODA_ERR_ALIGN;
+  return MODA_OK;
+}
+
 int validate_layout(const void* src, const void* dst, int B, int T, int L, int Hk, int d, int elem_bytes) {
   if (!src || !dst) return MODA_ERR_NULL;
   if (B <= 0 || T <= 0 || L <= 0 || Hk <= 0 || d <= 0) return MODA_ERR_SHAPE;
@@ -129,6 +154,26 @@ int moda_attn_decode_ring(const void* q, const void* k_cache, const void* v_cach
                           float* lse, void* workspace, size_t workspace_bytes, moda_stream_t stream) {
   return decode_common(q, k_cache, v_cache, k_depth, v_depth, B, T, Hq, Hk, d, S, L, out, lse, workspace,
                        workspace_bytes, stream);
+}
+
+int moda_attn_bwd(const void* q, const void* k_seq, const void* v_seq, const void* k_depth, const void* v_depth,
+                  const void* out, const float* lse, const void* dout, int B, int T, int Hq, int Hk, int d, int L,
+                  int causal, void* dq, void* dk_seq, void* dv_seq, void* dk_depth, void* dv_depth, void* workspace,
+                  size_t workspace_bytes, moda_stream_t stream) {
+  const int rc = validate_bwd(q, k_seq, v_seq, k_depth, v_depth, out, lse, dout, B, T, Hq, Hk, d, L, causal, dq,
+                              dk_seq, dv_seq, dk_depth, dv_depth, workspace, workspace_bytes);
+  if (rc != MODA_OK) return rc;
+  const bool depth = L > 0;
+  moda::BwdArgs a{q, k_seq, v_seq, depth ? k_depth : nullptr, depth ? v_depth : nullptr, out, lse, dout,
+                  B, T, Hq, Hk, d, L, causal, dq, dk_seq, dv_seq, depth ? dk_depth : nullptr,
+                  depth ? dv_depth : nullptr, workspace, stream};
+  return moda::launch_bwd_bf16(a) == hipSuccess ? MODA_OK : MODA_ERR_HIP;
+}
+
+size_t moda_attn_bwd_workspace(int B, int T, int Hq, int Hk, int d, int L) {
+  if (B <= 0 || T <= 0 || Hq <= 0 || Hk <= 0 || d <= 0 || L < 0) return 0;
+  if (Hq % Hk != 0) return 0;
+  return moda::bwd_workspace_bytes(B, T, Hq, d, L);
 }
 
 size_t moda_attn_decode_workspace(int B, int T, int Hq, int Hk, int d, int L) {

@@ -25,6 +25,17 @@ struct DecodeArgs {
   void* stream;
 };
 
+struct BwdArgs {
+  const void *q, *k, *v, *kd, *vd;  // forward inputs; depth packed [B][T][Hk][L][d]
+  const void* out;                  // forward output [B][T][Hq][d]
+  const float* lse;                 // forward lse [B][Hq][T], natural log
+  const void* dout;                 // output gradient [B][T][Hq][d]
+  int B, T, Hq, Hk, d, L, causal;
+  void *dq, *dk, *dv, *dkd, *dvd;   // gradients in the input layouts
+  void* workspace;
+  void* stream;
+};
+
 hipError_t launch_fwd_bf16(const FwdArgs& a);
 hipError_t launch_fwd_f32(const FwdArgs& a);
 int64_t fwd_bf16_grid_blocks(int B, int T, int Hq, int Hk);
@@ -33,6 +44,10 @@ int64_t fwd_f32_grid_blocks(int B, int T, int Hq);
 hipError_t launch_decode_bf16(const DecodeArgs& a);
 size_t decode_workspace_bytes(int B, int T, int Hq, int Hk, int d, int L);
 int64_t decode_grid_blocks(int B, int T, int Hk, int L);
+
+hipError_t launch_bwd_bf16(const BwdArgs& a);
+size_t bwd_workspace_bytes(int B, int T, int Hq, int d, int L);
+int64_t bwd_grid_blocks(int B, int T, int Hq, int Hk);
 
 hipError_t launch_pack_depth(const void* src, void* dst, int B, int T, int L, int Hk, int d, int elem_bytes,
                              void* stream);

@@ -152,5 +152,11 @@ def random_inputs(shape: Shape, seed: int, depth_aligned: bool = False, device="
     return make_inputs(shape, {n: seed + k for k, n in enumerate(TENSORS)}, depth_aligned, device)
 
 
+def random_dout(shape: Shape, seed: int, device="cpu"):
+    """An output gradient [B,T,Hq,d] for the backward: N(0, 1), rounded once to the working dtype."""
+    s = shape
+    return _randn((s.B, s.T, s.Hq, s.d), seed, device).to(_torch_dtype(s.dtype))
+
+
 def with_(shape: Shape, **kw) -> Shape:
     return replace(shape, **kw)

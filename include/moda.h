@@ -166,6 +166,58 @@ int moda_attn_decode_ring(const void* q, const void* k_cache, const void* v_cach
 size_t moda_attn_decode_workspace(int B, int T, int Hq, int Hk, int d, int L);
 
 /*
+ * MoDA backward, bf16 in / bf16 gradients, fp32 accumulation: the gradients of
+ * every input of moda_attn_fwd for the output gradient dout.  With the saved
+ * natural-log lse, each row's softmax weights are recomputed as
+ * P_n = exp(s <q, k_n> - lse) over the same candidates as the forward (the
+ * causally visible sequence keys of KV head hk and the L depth slots of the
+ * row's token; [Summ] 2.2 MoDA, [Notes] 二.2 unified softmax).  With
+ * dP_n = <dout, v_n>, Dsum = <dout, out> and dS_n = P_n (dP_n - Dsum):
+ *   dq  = s * sum_n dS_n k_n
+ *   dk_n = s * sum over the rows that see n of dS_n q,  dv_n = sum of P_n dout.
+ * A sequence key collects from every row of its G heads at or after it (all
+ * rows when causal == 0); a depth slot only from the G rows of its own token.
+ *
+ * Arguments
+ *   q, k_seq, v_seq, k_depth, v_depth, B, T, Hq, Hk, d, L, causal: the forward's
+ *            inputs exactly as given to moda_attn_fwd (depth packed
+ *            [B][T][Hk][L][d]; NULL iff L == 0).
+ *   out      [B][T][Hq][d] bf16: the forward's output for these inputs.
+ *   lse      [B][Hq][T] fp32: the forward's lse for these inputs.
+ *   dout     [B][T][Hq][d] bf16: gradient of the loss with respect to out.
+ *   dq       [B][T][Hq][d] bf16 (written).
+ *   dk_seq, dv_seq     [B][T][Hk][d] bf16 (written).
+ *   dk_depth, dv_depth [B][T][Hk][L][d] bf16, packed like k_depth (written;
+ *            may be NULL iff L == 0).
+ *   workspace  device memory of at least moda_attn_bwd_workspace(...) bytes,
+ *            owned by the caller, 16-byte aligned; per-row statistics and
+ *            the depth share of dq live there during the call (contents on
+ *            entry ignored, on return unspecified).  Calls that share a
+ *            workspace must not overlap in time.
+ *   workspace_bytes  its size.
+ * Gradient buffers must not alias the inputs or each other.  Every gradient
+ * element is produced by one lane in a fixed order (no atomics): results are
+ * deterministic.  Enqueued on `stream`; nothing is allocated or synchronised.
+ *
+ * Errors: MODA_ERR_NULL (a required pointer NULL; depth inputs or gradients
+ * NULL with L > 0); MODA_ERR_SHAPE (a size <= 0, L < 0, Hq % Hk != 0,
+ * causal not 0/1, or workspace_bytes below moda_attn_bwd_workspace);
+ * MODA_ERR_UNSUPPORTED (d not 64 or 128; G not in {1,2,4,8,16}; (T + 128) *
+ * Hq * d * 2 bytes or a grid beyond 2^31); MODA_ERR_ALIGN; MODA_ERR_HIP.
+ */
+int moda_attn_bwd(const void* q, const void* k_seq, const void* v_seq, const void* k_depth, const void* v_depth,
+                  const void* out, const float* lse, const void* dout, int B, int T, int Hq, int Hk, int d, int L,
+                  int causal, void* dq, void* dk_seq, void* dv_seq, void* dk_depth, void* dv_depth, void* workspace,
+                  size_t workspace_bytes, moda_stream_t stream);
+
+/*
+ * Workspace bytes moda_attn_bwd needs for these sizes (host only; 0 when a size
+ * is invalid): two fp32 values per query row, plus d fp32 values per query
+ * row when L > 0, each region rounded up to 256 bytes.
+ */
+size_t moda_attn_bwd_workspace(int B, int T, int Hq, int Hk, int d, int L);
+
+/*
  * Depth-stream pack: dst[b][t][hk][l][:] = src[b][t][l][hk][:], bit for bit.
  *
  * [Summ] 3.2 stores a position's L depth states contiguously; this layout

@@ -144,3 +144,40 @@ def test_ring_validation(lib):
                                                  lib.moda_attn_decode_workspace(1, 300, 8, 2, 128, max(L, 0)), None)
     assert dec(4, 5) == api.MODA_ERR_SHAPE
     assert dec(4, -1) == api.MODA_ERR_SHAPE
+
+
+def bwd(lib, q=A, k=A, v=A, kd=A, vd=A, out=A, lse=A, do=A, B=2, T=300, Hq=8, Hk=2, d=128, L=5, causal=1,
+        dq=A, dk=A, dv=A, dkd=A, dvd=A, ws=A2, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.moda_attn_bwd_workspace(B, T, Hq, Hk, d, L)
+    return lib.moda_attn_bwd(q, k, v, kd, vd, out, lse, do, B, T, Hq, Hk, d, L, causal, dq, dk, dv, dkd, dvd,
+                             ws, ws_bytes, None)
+
+
+def test_bwd_workspace_size(lib):
+    # lse2 and Dsum (fp32 per query row), plus the fp32 depth share of dq when L > 0;
+    # each region rounded up to 256 bytes.
+    r = lambda n: (n + 255) // 256 * 256  # noqa: E731
+    assert lib.moda_attn_bwd_workspace(2, 300, 8, 2, 128, 5) == 2 * r(2 * 300 * 8 * 4) + r(2 * 300 * 8 * 128 * 4)
+    assert lib.moda_attn_bwd_workspace(2, 300, 8, 2, 128, 0) == 2 * r(2 * 300 * 8 * 4)
+    assert lib.moda_attn_bwd_workspace(1, 65536, 16, 4, 128, 48) == 2 * 65536 * 16 * 4 + 65536 * 16 * 128 * 4
+    assert lib.moda_attn_bwd_workspace(0, 256, 4, 4, 64, 0) == 0
+    assert lib.moda_attn_bwd_workspace(1, 256, 4, 4, 64, -1) == 0
+    assert lib.moda_attn_bwd_workspace(1, 256, 6, 4, 64, 0) == 0
+
+
+def test_bwd_validation(lib):
+    null = ctypes.c_void_p(0)
+    for name in ("q", "k", "v", "out", "lse", "do", "dq", "dk", "dv", "ws", "kd", "vd", "dkd", "dvd"):
+        assert bwd(lib, **{name: null}) == api.MODA_ERR_NULL, name
+    # depth pointers may be NULL when L == 0
+    assert bwd(lib, L=0, kd=null, vd=null, dkd=null, dvd=null, ws=MIS) == api.MODA_ERR_ALIGN
+    for kw in (dict(B=0), dict(T=0), dict(Hq=0), dict(Hk=0), dict(d=0), dict(L=-1), dict(Hq=6, Hk=4),
+               dict(causal=2)):
+        assert bwd(lib, **kw) == api.MODA_ERR_SHAPE, kw
+    assert bwd(lib, ws_bytes=lib.moda_attn_bwd_workspace(2, 300, 8, 2, 128, 5) - 4) == api.MODA_ERR_SHAPE
+    # G = 32 has a forward but no backward; sizes beyond the 32-bit offsets are refused
+    for kw in (dict(d=96), dict(Hq=6, Hk=2), dict(Hq=64, Hk=2), dict(T=1 << 20, Hq=16, Hk=2)):
+        assert bwd(lib, **kw) == api.MODA_ERR_UNSUPPORTED, kw
+    for name in ("q", "k", "v", "kd", "vd", "out", "lse", "do", "dq", "dk", "dv", "dkd", "dvd", "ws"):
+        assert bwd(lib, **{name: MIS}) == api.MODA_ERR_ALIGN, name
