@@ -69,6 +69,25 @@ __device__ __forceinline__ s16x4 read_tr(uint32_t addr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_at<lds_s16x4_t>(addr));
 }
 
+// Transposed LDS reads issued as inline asm.  As a compiler builtin every such
+// read first waits for all outstanding direct-to-LDS loads (the compiler
+// cannot tell that those fill the other buffer), which exposes the next
+// tile's load latency in every tile.  The compiler does not track these
+// reads, so their consumers must follow lds_ready() on the same values.
+__device__ __forceinline__ s16x4 read_tr_async(uint32_t addr) {
+  s16x4 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
+  return r;
+}
+// Wait until every LDS read of this wave has returned; afterwards the values
+// passed here may be used (each is re-defined after the wait).
+template <int N>
+__device__ __forceinline__ void lds_ready(bf16x8 (&x)[N]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(x[i]));
+}
+
 // ---- 64-row tiles read both row-wise and transposed -----------------------------
 //
 // Logical 16-byte chunk c of tile row r lives at physical chunk c ^ swz_u(r),
@@ -583,17 +602,55 @@ __device__ __forceinline__ void dma_rows(const uint16_t* qb, const uint16_t* ob,
 }
 
 // One 64-row tile against the wave's 32 keys: for both 32-row blocks S = Q K^T,
-// dP = dO V^T, P and dS, then dV^T += dO^T P and dK^T += Q^T dS.
+// dP = dO V^T, P and dS, then dV^T += dO^T P and dK^T += Q^T dS.  LDS operands
+// are fetched in groups ahead of the products that use them (the next block's
+// row operands while this block's weights are formed), so each product waits
+// on one group's latency, not on one read's per MFMA.
+template <int D>
+__device__ __forceinline__ void load_rows(bf16x8 (&aq)[D / 16], bf16x8 (&ao)[D / 16], const TileReads<D>& qa,
+                                          int off, int do_off) {
+#pragma unroll
+  for (int sl = 0; sl < D / 16; ++sl) {
+    aq[sl] = *lds_at<lds_bf16x8_t>(qa.nr[sl] + off);
+    ao[sl] = *lds_at<lds_bf16x8_t>(qa.nr[sl] + off + do_off);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ bf16x8 read_tr8(const TileReads<D>& ta, int dt, int off) {
+  const s16x4 lo4 = read_tr_async(ta.lo[dt] + off);
+  const s16x4 hi4 = read_tr_async(ta.hi[dt] + off);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 template <int D, bool MASK>
 __device__ __forceinline__ void kv_tile(f32x16 (&dka)[D / 32], f32x16 (&dva)[D / 32], const bf16x8 (&kf)[D / 16],
-                                        const bf16x8 (&vf)[D / 16], const TileReads<D>& qa, const TileReads<D>& oa,
-                                        uint32_t stat, int r0, int lgG, int my_key, int half, float scale_log2) {
+                                        const bf16x8 (&vf)[D / 16], const TileReads<D>& qa, uint32_t stat, int r0,
+                                        int lgG, int my_key, int half, float scale_log2) {
   using TL = Tile<D>;
   using RS = RowStage<D>;
+  constexpr int DO = RS::DO - RS::Q;
+  bf16x8 aq[D / 16], ao[D / 16];
+  load_rows<D>(aq, ao, qa, 0, DO);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const f32x16 s = qk_block<D>(kf, qa.nr, 32 * j * TL::ROW_BYTES);   // [row][key]
-    const f32x16 dp = qk_block<D>(vf, oa.nr, 32 * j * TL::ROW_BYTES);
+    f32x16 s = {}, dp = {};
+#pragma unroll
+    for (int sl = 0; sl < D / 16; ++sl) {
+      s = mfma32(aq[sl], kf[sl], s);     // [row][key]
+      dp = mfma32(ao[sl], vf[sl], dp);
+    }
+    bf16x8 tt[4 * (D / 32)];  // [h][dO, Q][dt]
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        tt[(2 * h) * (D / 32) + dt] = read_tr8<D>(qa, dt, (32 * j + 16 * h) * TL::ROW_BYTES + DO);
+        tt[(2 * h + 1) * (D / 32) + dt] = read_tr8<D>(qa, dt, (32 * j + 16 * h) * TL::ROW_BYTES);
+      }
+    if (j == 0) load_rows<D>(aq, ao, qa, 32 * TL::ROW_BYTES, DO);
+    __builtin_amdgcn_sched_barrier(0);
     float p[16], ds[16];
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
@@ -612,11 +669,14 @@ __device__ __forceinline__ void kv_tile(f32x16 (&dka)[D / 32], f32x16 (&dva)[D /
     bf16x8 pb[2], db[2];
     pack16(p, pb);
     pack16(ds, db);
+    lds_ready(tt);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      acc_group<D>(dva, pb[h], oa, (32 * j + 16 * h) * TL::ROW_BYTES);
-      acc_group<D>(dka, db[h], qa, (32 * j + 16 * h) * TL::ROW_BYTES);
-    }
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        dva[dt] = mfma32(tt[(2 * h) * (D / 32) + dt], pb[h], dva[dt]);
+        dka[dt] = mfma32(tt[(2 * h + 1) * (D / 32) + dt], db[h], dka[dt]);
+      }
   }
 }
 
@@ -689,16 +749,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
     const int r0 = it * kBN;
     if (((r0 + kBN - 1) >> lgG) < kw0) continue;  // no row of this tile sees the wave's keys
     const uint32_t base = lds_addr(cur);
-    kv_tile<D, true>(dka, dva, kf, vf, at<D>(ro, base + RS::Q), at<D>(ro, base + RS::DO), base, r0, lgG, my_key,
-                     half, scale_log2);
+    kv_tile<D, true>(dka, dva, kf, vf, at<D>(ro, base + RS::Q), base, r0, lgG, my_key, half, scale_log2);
   }
   for (; it < nt; ++it, ++pos) {  // unmasked tiles
     lds_u8* cur = buf_of(pos);
     publish_tile();
     if (it + 1 < nt) dma_rows<D>(qb, ob, l2b, ddb, T, Hq, lgG, TG, it + 1, buf_of(pos + 1), wave, lane, dm);
     const uint32_t base = lds_addr(cur);
-    kv_tile<D, false>(dka, dva, kf, vf, at<D>(ro, base + RS::Q), at<D>(ro, base + RS::DO), base, it * kBN, lgG,
-                      my_key, half, scale_log2);
+    kv_tile<D, false>(dka, dva, kf, vf, at<D>(ro, base + RS::Q), base, it * kBN, lgG, my_key, half, scale_log2);
   }
 
   if (my_key < T) {
