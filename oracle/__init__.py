@@ -8,6 +8,7 @@ from .oracle import (  # noqa: F401
     moda_fwd,
     moda_fwd_rows,
     moda_bwd,
+    moda_bwd_sampled,
     pack_depth,
     append_depth_slot,
     default_threads,

@@ -395,6 +395,222 @@ int moda_oracle_bwd(const void* q, const void* k_seq, const void* v_seq, const v
   return failed ? -5 : 0;
 }
 
+/* ---- sampled gradients -------------------------------------------------------
+ *
+ * The same gradients as moda_oracle_bwd, for selected outputs only, so that
+ * long sequences can be checked without the full quadratic cost:
+ *   rows  (b, t, h)   -> dq[b, t, h, :]
+ *   keys  (b, j, hk)  -> dk[b, j, hk, :], dv[b, j, hk, :]  (sequence keys)
+ *   toks  (b, t, hk)  -> dkd[b, t, :, hk, :], dvd[b, t, :, hk, :]  (all L slots)
+ * Each contributing row is evaluated exactly as in moda_oracle_bwd: its full
+ * softmax over all its candidates, dP, D and dS.  A key collects from every row
+ * that sees it, a depth slot from the G rows of its own token. */
+
+/* P and dS of every candidate of row (b, t, h): P in P_out[0 .. nseq+L), dS in
+ * dS_out; qrow / dorow receive the row's q and dout.  Returns nseq. */
+static int orc_row_grad(const orc_problem* p, const void* dout, int b, int t, int h, double* P_out,
+                        double* dS_out, double* qrow, double* dorow) {
+  const int G = p->Hq / p->Hk, hk = h / G, d = p->d, L = p->L;
+  const double s = 1.0 / sqrt((double)p->d);
+  const int nseq = p->causal ? 1 + t : p->T;
+  const int ncand = nseq + L;
+  for (int c = 0; c < d; ++c) {
+    qrow[c] = orc_load(p->q, ix_q(p, b, t, h, c), p->kind);
+    dorow[c] = orc_load(dout, ix_q(p, b, t, h, c), p->kind);
+  }
+  double m = -INFINITY;
+  for (int n = 0; n < ncand; ++n) {
+    double dot = 0.0, dpv = 0.0;
+    for (int c = 0; c < d; ++c) {
+      const size_t kix = n < nseq ? ix_kv(p, b, n, hk, c) : ix_depth(p, b, t, n - nseq, hk, c);
+      dot += qrow[c] * orc_load(n < nseq ? p->k_seq : p->k_depth, kix, p->kind);
+      dpv += dorow[c] * orc_load(n < nseq ? p->v_seq : p->v_depth, kix, p->kind);
+    }
+    P_out[n] = s * dot;
+    dS_out[n] = dpv; /* dP for now */
+    if (P_out[n] > m) m = P_out[n];
+  }
+  double Z = 0.0;
+  for (int n = 0; n < ncand; ++n) {
+    P_out[n] = exp(P_out[n] - m);
+    Z += P_out[n];
+  }
+  double D = 0.0;
+  for (int n = 0; n < ncand; ++n) {
+    P_out[n] /= Z;
+    D += P_out[n] * dS_out[n];
+  }
+  for (int n = 0; n < ncand; ++n) dS_out[n] = P_out[n] * (dS_out[n] - D);
+  return nseq;
+}
+
+typedef struct {
+  const orc_problem* p;
+  const void* dout;
+  const int* work; /* triples (b, t, h) */
+  long long first, last;
+  const int *rows, *keys, *toks;
+  long long nrows, nkeys, ntoks;
+  double *dq, *dk, *dv, *dkd, *dvd; /* this thread's accumulators */
+} orc_samp_job;
+
+static void* orc_samp_worker(void* arg) {
+  orc_samp_job* j = (orc_samp_job*)arg;
+  const orc_problem* p = j->p;
+  const int d = p->d, L = p->L, G = p->Hq / p->Hk;
+  const double s = 1.0 / sqrt((double)p->d);
+  double* w = (double*)malloc(sizeof(double) * (2 * ((size_t)p->T + L) + 2 * (size_t)d));
+  if (!w) return (void*)1;
+  double *P = w, *dS = w + p->T + L, *qrow = w + 2 * ((size_t)p->T + L), *dorow = qrow + d;
+  for (long long r = j->first; r < j->last; ++r) {
+    const int b = j->work[3 * r], t = j->work[3 * r + 1], h = j->work[3 * r + 2], hk = h / G;
+    const int nseq = orc_row_grad(p, j->dout, b, t, h, P, dS, qrow, dorow);
+    for (long long i = 0; i < j->nrows; ++i) /* dq of a sampled row */
+      if (j->rows[3 * i] == b && j->rows[3 * i + 1] == t && j->rows[3 * i + 2] == h)
+        for (int c = 0; c < d; ++c) {
+          double acc = 0.0;
+          for (int n = 0; n < nseq + L; ++n) {
+            const size_t kix = n < nseq ? ix_kv(p, b, n, hk, c) : ix_depth(p, b, t, n - nseq, hk, c);
+            acc += dS[n] * orc_load(n < nseq ? p->k_seq : p->k_depth, kix, p->kind);
+          }
+          j->dq[i * d + c] += s * acc;
+        }
+    for (long long i = 0; i < j->nkeys; ++i) { /* sampled sequence keys this row sees */
+      const int kb = j->keys[3 * i], kj = j->keys[3 * i + 1], khk = j->keys[3 * i + 2];
+      if (kb != b || khk != hk || kj >= nseq) continue;
+      for (int c = 0; c < d; ++c) {
+        j->dk[i * d + c] += s * dS[kj] * qrow[c];
+        j->dv[i * d + c] += P[kj] * dorow[c];
+      }
+    }
+    for (long long i = 0; i < j->ntoks; ++i) { /* depth slots of a sampled token */
+      if (j->toks[3 * i] != b || j->toks[3 * i + 1] != t || j->toks[3 * i + 2] != hk) continue;
+      for (int l = 0; l < L; ++l)
+        for (int c = 0; c < d; ++c) {
+          j->dkd[(i * L + l) * d + c] += s * dS[nseq + l] * qrow[c];
+          j->dvd[(i * L + l) * d + c] += P[nseq + l] * dorow[c];
+        }
+    }
+  }
+  free(w);
+  return NULL;
+}
+
+int moda_oracle_bwd_sampled(const void* q, const void* k_seq, const void* v_seq, const void* k_depth,
+                            const void* v_depth, const void* dout, int kind, int B, int T, int Hq, int Hk, int d,
+                            int L, int causal, const int* rows, long long nrows, double* dq_rows, const int* keys,
+                            long long nkeys, double* dk_keys, double* dv_keys, const int* toks, long long ntoks,
+                            double* dkd_toks, double* dvd_toks, int nthreads) {
+  orc_problem p = {q, k_seq, v_seq, k_depth, v_depth, kind, B, T, Hq, Hk, d, L, causal};
+  int rc = orc_check(&p);
+  if (rc) return rc;
+  if (!dout || nrows < 0 || nkeys < 0 || ntoks < 0) return -1;
+  if ((nrows && (!rows || !dq_rows)) || (nkeys && (!keys || !dk_keys || !dv_keys)) ||
+      (ntoks && L > 0 && (!toks || !dkd_toks || !dvd_toks)))
+    return -1;
+  const int G = Hq / Hk;
+  for (long long i = 0; i < nrows; ++i)
+    if (rows[3 * i] < 0 || rows[3 * i] >= B || rows[3 * i + 1] < 0 || rows[3 * i + 1] >= T || rows[3 * i + 2] < 0 ||
+        rows[3 * i + 2] >= Hq)
+      return -2;
+  for (long long i = 0; i < nkeys + ntoks; ++i) {
+    const int* e = i < nkeys ? keys + 3 * i : toks + 3 * (i - nkeys);
+    if (e[0] < 0 || e[0] >= B || e[1] < 0 || e[1] >= T || e[2] < 0 || e[2] >= Hk) return -2;
+  }
+  /* Mark every row that contributes to a requested output. */
+  unsigned char* need = (unsigned char*)calloc((size_t)B * T * Hq, 1);
+  if (!need) return -5;
+#define NEED(b, t, h) need[((size_t)(b) * T + (t)) * Hq + (h)]
+  for (long long i = 0; i < nrows; ++i) NEED(rows[3 * i], rows[3 * i + 1], rows[3 * i + 2]) = 1;
+  for (long long i = 0; i < nkeys; ++i)
+    for (int t = causal ? keys[3 * i + 1] : 0; t < T; ++t)
+      for (int g = 0; g < G; ++g) NEED(keys[3 * i], t, keys[3 * i + 2] * G + g) = 1;
+  for (long long i = 0; i < ntoks; ++i)
+    for (int g = 0; g < G; ++g) NEED(toks[3 * i], toks[3 * i + 1], toks[3 * i + 2] * G + g) = 1;
+  long long nwork = 0;
+  for (size_t i = 0; i < (size_t)B * T * Hq; ++i) nwork += need[i];
+  int* work = (int*)malloc(sizeof(int) * 3 * (size_t)(nwork > 0 ? nwork : 1));
+  if (!work) {
+    free(need);
+    return -5;
+  }
+  long long wi = 0;
+  for (int b = 0; b < B; ++b)
+    for (int t = 0; t < T; ++t)
+      for (int h = 0; h < Hq; ++h)
+        if (NEED(b, t, h)) {
+          work[3 * wi] = b;
+          work[3 * wi + 1] = t;
+          work[3 * wi + 2] = h;
+          ++wi;
+        }
+#undef NEED
+  free(need);
+  if (nthreads < 1) nthreads = 1;
+  if (nwork < nthreads) nthreads = nwork > 0 ? (int)nwork : 1;
+  const size_t nq = (size_t)nrows * d, nk = (size_t)nkeys * d, nt = (size_t)ntoks * L * d;
+  const size_t per = nq + 2 * nk + 2 * nt;
+  double* acc = (double*)calloc((size_t)nthreads * (per > 0 ? per : 1), sizeof(double));
+  pthread_t* tid = (pthread_t*)malloc(sizeof(pthread_t) * nthreads);
+  orc_samp_job* jobs = (orc_samp_job*)malloc(sizeof(orc_samp_job) * nthreads);
+  if (!acc || !tid || !jobs) {
+    free(acc);
+    free(tid);
+    free(jobs);
+    free(work);
+    return -5;
+  }
+  for (int w = 0; w < nthreads; ++w) {
+    double* a = acc + (size_t)w * per;
+    orc_samp_job jb = {&p, dout, work, nwork * w / nthreads, nwork * (w + 1) / nthreads, rows, keys, toks, nrows,
+                       nkeys, L > 0 ? ntoks : 0, a, a + nq, a + nq + nk, a + nq + 2 * nk, a + nq + 2 * nk + nt};
+    jobs[w] = jb;
+  }
+  int failed = 0;
+  for (int w = 1; w < nthreads; ++w)
+    if (pthread_create(&tid[w], NULL, orc_samp_worker, &jobs[w]) != 0) {
+      tid[w] = 0;
+      if (orc_samp_worker(&jobs[w]) != NULL) failed = 1;
+    }
+  if (orc_samp_worker(&jobs[0]) != NULL) failed = 1;
+  for (int w = 1; w < nthreads; ++w) {
+    void* res = NULL;
+    if (tid[w]) {
+      pthread_join(tid[w], &res);
+      if (res != NULL) failed = 1;
+    }
+  }
+  /* Reduce the per-thread partial sums in thread order. */
+  for (size_t e = 0; e < nq; ++e) {
+    double x = 0.0;
+    for (int w = 0; w < nthreads; ++w) x += jobs[w].dq[e];
+    dq_rows[e] = x;
+  }
+  for (size_t e = 0; e < nk; ++e) {
+    double x = 0.0, y = 0.0;
+    for (int w = 0; w < nthreads; ++w) {
+      x += jobs[w].dk[e];
+      y += jobs[w].dv[e];
+    }
+    dk_keys[e] = x;
+    dv_keys[e] = y;
+  }
+  for (size_t e = 0; e < nt; ++e) {
+    double x = 0.0, y = 0.0;
+    for (int w = 0; w < nthreads; ++w) {
+      x += jobs[w].dkd[e];
+      y += jobs[w].dvd[e];
+    }
+    dkd_toks[e] = x;
+    dvd_toks[e] = y;
+  }
+  free(acc);
+  free(tid);
+  free(jobs);
+  free(work);
+  return failed ? -5 : 0;
+}
+
 /* Depth-stream packing, by definition: dst[b][t][hk][l][:] = src[b][t][l][hk][:]
  * for elements of elem_bytes bytes.  This is the reorganisation that keeps
  * each position's L depth states together ([Summ] 3.2), with the KV head

@@ -34,6 +34,9 @@ def _load():
         lib.moda_oracle_fwd_rows.restype = i32
         lib.moda_oracle_bwd.argtypes = [vp] * 6 + [i32] * 8 + [vp] * 5 + [i32]
         lib.moda_oracle_bwd.restype = i32
+        lib.moda_oracle_bwd_sampled.argtypes = ([vp] * 6 + [i32] * 8 + [vp, i64, vp, vp, i64, vp, vp, vp, i64, vp, vp]
+                                                + [i32])
+        lib.moda_oracle_bwd_sampled.restype = i32
         lib.moda_oracle_pack_depth.argtypes = [vp, vp] + [i32] * 6
         lib.moda_oracle_pack_depth.restype = i32
         lib.moda_oracle_append_depth_slot.argtypes = [vp, vp] + [i32] * 7
@@ -151,6 +154,33 @@ def moda_bwd(q, k_seq, v_seq, k_depth, v_depth, dout, causal=True, nthreads=None
                              nthreads or default_threads())
     if rc != 0:
         raise RuntimeError("moda_oracle_bwd failed with code %d" % rc)
+    return dq, dk, dv, dkd, dvd
+
+
+def moda_bwd_sampled(q, k_seq, v_seq, k_depth, v_depth, dout, rows=(), keys=(), toks=(), causal=True,
+                     nthreads=None):
+    """Selected gradients in fp64: rows [n,3] (b, t, h) -> dq [n,d]; keys [m,3] (b, j, hk) ->
+    (dk, dv) [m,d] of sequence key j; toks [r,3] (b, t, hk) -> (dkd, dvd) [r,L,d] of token t's
+    depth slots.  Returns (dq, dk, dv, dkd, dvd)."""
+    lib = _load()
+    (qa, ka, va, kda, vda), kind, (B, T, Hq, Hk, d, L) = _prepare(q, k_seq, v_seq, k_depth, v_depth)
+    da, dkind = _host(dout)
+    if dkind != kind or da.shape != qa.shape:
+        raise ValueError("dout must be [B,T,Hq,d] with the inputs' dtype")
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int32).reshape(-1, 3))
+    kk = np.ascontiguousarray(np.asarray(keys, dtype=np.int32).reshape(-1, 3))
+    tt = np.ascontiguousarray(np.asarray(toks, dtype=np.int32).reshape(-1, 3))
+    dq = np.zeros((r.shape[0], d))
+    dk = np.zeros((kk.shape[0], d))
+    dv = np.zeros((kk.shape[0], d))
+    dkd = np.zeros((tt.shape[0], L, d))
+    dvd = np.zeros((tt.shape[0], L, d))
+    rc = lib.moda_oracle_bwd_sampled(_ptr(qa), _ptr(ka), _ptr(va), _ptr(kda), _ptr(vda), _ptr(da), kind,
+                                     B, T, Hq, Hk, d, L, int(bool(causal)),
+                                     _ptr(r), r.shape[0], _ptr(dq), _ptr(kk), kk.shape[0], _ptr(dk), _ptr(dv),
+                                     _ptr(tt), tt.shape[0], _ptr(dkd), _ptr(dvd), nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError("moda_oracle_bwd_sampled failed with code %d" % rc)
     return dq, dk, dv, dkd, dvd
 
 

@@ -319,3 +319,26 @@ def pin_bwd_invariants(seed):
     # zero output gradient -> every gradient zero
     z = oracle.moda_bwd(q, k, v, kd, vd, torch.zeros_like(dout), nthreads=2)
     assert all(np.abs(x).max() == 0.0 for x in z)
+
+
+def pin_bwd_sampled(seed, causal=True, tol=1e-11):
+    """Selected gradients (rows' dq, keys' dk/dv, tokens' depth gradients) equal torch autograd's."""
+    B, T, Hq, Hk, d, L = 2, 11, 4, 2, 8, 3
+    q, k, v, kd, vd = rand_problem(B, T, Hq, Hk, d, L, seed)
+    dout = torch.randn(B, T, Hq, d, generator=torch.Generator("cpu").manual_seed(seed + 13), dtype=torch.float64)
+    rows = [(0, 0, 0), (1, 5, 3), (0, T - 1, 2), (1, T - 1, 1)]
+    keys = [(0, 0, 0), (1, 4, 1), (0, T - 1, 1), (1, T - 2, 0)]
+    toks = [(0, 0, 1), (1, 7, 0), (1, T - 1, 1)]
+    dq, dk, dv, dkd, dvd = oracle.moda_bwd_sampled(q, k, v, kd, vd, dout, rows, keys, toks, causal=causal,
+                                                   nthreads=3)
+    wq, wk, wv, wkd, wvd = autograd_reference(q, k, v, kd, vd, dout, causal)
+    G = Hq // Hk
+    for i, (b, t, h) in enumerate(rows):
+        assert np.abs(dq[i] - wq[b, t, h]).max() <= tol, "sampled dq row differs from autograd"
+    for i, (b, j, hk) in enumerate(keys):
+        assert np.abs(dk[i] - wk[b, j, hk]).max() <= tol, "sampled dk differs from autograd"
+        assert np.abs(dv[i] - wv[b, j, hk]).max() <= tol, "sampled dv differs from autograd"
+    for i, (b, t, hk) in enumerate(toks):
+        assert np.abs(dkd[i] - wkd[b, t, :, hk]).max() <= tol, "sampled depth dk differs from autograd"
+        assert np.abs(dvd[i] - wvd[b, t, :, hk]).max() <= tol, "sampled depth dv differs from autograd"
+    assert G == 2

@@ -161,3 +161,26 @@ def test_bwd_thread_count_and_bf16_widening():
     d = oracle.moda_bwd(*[x.double() for x in bf], nthreads=2)
     for x, y in zip(c, d):
         assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_bwd_sampled_matches_autograd(causal):
+    pins.pin_bwd_sampled(350, causal=causal)
+
+
+def test_bwd_sampled_equals_full_oracle():
+    q, k, v, kd, vd = rand_problem(1, 40, 8, 2, 16, 5, 360)
+    dout = torch.randn(1, 40, 8, 16, generator=torch.Generator("cpu").manual_seed(361), dtype=torch.float64)
+    full = oracle.moda_bwd(q, k, v, kd, vd, dout, nthreads=2)
+    rows = [(0, t, h) for t in (0, 17, 39) for h in (0, 5, 7)]
+    keys = [(0, j, hk) for j in (0, 20, 38, 39) for hk in (0, 1)]
+    toks = [(0, t, hk) for t in (0, 33) for hk in (0, 1)]
+    dq, dk, dv, dkd, dvd = oracle.moda_bwd_sampled(q, k, v, kd, vd, dout, rows, keys, toks, nthreads=4)
+    for i, (b, t, h) in enumerate(rows):
+        assert np.abs(dq[i] - full[0][b, t, h]).max() <= 1e-13
+    for i, (b, j, hk) in enumerate(keys):
+        assert np.abs(dk[i] - full[1][b, j, hk]).max() <= 1e-13
+        assert np.abs(dv[i] - full[2][b, j, hk]).max() <= 1e-13
+    for i, (b, t, hk) in enumerate(toks):
+        assert np.abs(dkd[i] - full[3][b, t, :, hk]).max() <= 1e-13
+        assert np.abs(dvd[i] - full[4][b, t, :, hk]).max() <= 1e-13

@@ -41,6 +41,11 @@ MUTANTS = {
     "bwd_causal_sees_all": ("const int nseq = p->causal ? t + 1 : T;", "const int nseq = T;"),
     "bwd_interleaved_head_map": ("const int h = hk * G + g;", "const int h = g * p->Hk + hk;"),
     "bwd_unnormalised_weights": ("logit[n] /= Z; /* P_n */", "logit[n] /= Z * Z; /* P_n */"),
+    "sampled_dk_unscaled": ("j->dk[i * d + c] += s * dS[kj] * qrow[c];", "j->dk[i * d + c] += dS[kj] * qrow[c];"),
+    "sampled_depth_slot_shift": ("j->dvd[(i * L + l) * d + c] += P[nseq + l] * dorow[c];",
+                                 "j->dvd[(i * L + l) * d + c] += P[nseq + l - (l > 0)] * dorow[c];"),
+    "sampled_missing_row_correction": ("for (int n = 0; n < ncand; ++n) dS_out[n] = P_out[n] * (dS_out[n] - D);",
+                                       "for (int n = 0; n < ncand; ++n) dS_out[n] = P_out[n] * dS_out[n];"),
 }
 
 ALL_PINS = [
@@ -58,6 +63,8 @@ ALL_PINS = [
     lambda: pins.pin_bwd_l0_gqa(1, 11, 4, 2, 8, True, 111),
     lambda: pins.pin_bwd_finite_difference(112),
     lambda: pins.pin_bwd_invariants(113),
+    lambda: pins.pin_bwd_sampled(114),
+    lambda: pins.pin_bwd_sampled(115, causal=False),
 ]
 
 
@@ -77,8 +84,8 @@ def _build_mutant(tmp_path, name):
 def test_pins_reject_planted_mistake(tmp_path, monkeypatch, name):
     good = orc._load()
     mutant = ctypes.CDLL(_build_mutant(tmp_path, name))
-    for fn in ("moda_oracle_fwd", "moda_oracle_fwd_rows", "moda_oracle_bwd", "moda_oracle_pack_depth",
-               "moda_oracle_append_depth_slot"):
+    for fn in ("moda_oracle_fwd", "moda_oracle_fwd_rows", "moda_oracle_bwd", "moda_oracle_bwd_sampled",
+               "moda_oracle_pack_depth", "moda_oracle_append_depth_slot"):
         getattr(mutant, fn).argtypes = getattr(good, fn).argtypes
         getattr(mutant, fn).restype = getattr(good, fn).restype
     monkeypatch.setattr(orc, "_lib", mutant)
