@@ -102,6 +102,9 @@ def _kernel_label(name):
         return "moda_decode partial"
     if "moda_decode_merge_kernel" in name:
         return "moda_decode merge"
+    for k in ("rows", "depth", "dq", "dkv"):
+        if "moda_bwd_%s_kernel" % k in name:
+            return "moda_bwd %s" % k
     return None
 
 
@@ -154,6 +157,47 @@ def _decode_summary(stats, counters, f_scale, w_scale, command):
         wr = counters["WRITE_SIZE"].get(lab, 0.0) * w_scale
         lines.append("  %-22s read %.4g B  write %.4g B" % (lab, rd, wr))
     with open(os.path.join(os.path.dirname(TRAFFIC_FILE), "moda_decode_b16_t64k.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def _bwd_summary(stats, counters, f_scale, w_scale, command):
+    """profiles/moda_bwd_long_L48.txt: the backward kernels of the same bench run."""
+    shape = I.workload(5, 0)
+    B, T, Hq, Hk, d, L = shape.B, shape.T, shape.Hq, shape.Hk, shape.d, shape.L
+    P = acc.visible_pairs(T, True)
+    # Products each kernel executes (2*d flops per pair each): dq recomputes S and dP, then dS K;
+    # dkv computes S, dP, then P^T dO and dS^T Q; depth does all five (and S, dP twice) on 16-row tiles.
+    f_dq, f_dkv = 6 * d * B * Hq * P, 8 * d * B * Hq * P
+    b_depth = 2 * acc.depth_bytes(shape) + 2 * B * T * Hq * d * 2 + B * T * Hq * d * 4
+    lines = ["# rocprofv3 summary: MoDA backward, long-context layer B=%d T=%d Hq=%d Hk=%d d=%d, L=%d and L=0, bf16"
+             % (B, T, Hq, Hk, d, L), "",
+             "kernel trace (rocprofv3 --kernel-trace --stats):", "  command: " + command[0], "",
+             "  %-22s %6s %12s %12s %12s" % ("kernel", "calls", "avg ms", "min ms", "max ms")]
+    for lab in ("moda_bwd rows", "moda_bwd depth", "moda_bwd dq", "moda_bwd dkv"):
+        if lab in stats:
+            n, avg, mn, mx = stats[lab]
+            lines.append("  %-22s %6d %12.4f %12.4f %12.4f" % (lab, n, avg, mn, mx))
+    lines.append("")
+    if "moda_bwd dq" in stats:
+        lines.append("  dq:  %.1f TFLOP/s of its three products (%.4g flop)" % (f_dq / stats["moda_bwd dq"][1] / 1e9,
+                                                                             f_dq))
+    if "moda_bwd dkv" in stats:
+        lines.append("  dkv: %.1f TFLOP/s of its four products (%.4g flop)"
+                     % (f_dkv / stats["moda_bwd dkv"][1] / 1e9, f_dkv))
+    if "moda_bwd depth" in stats:
+        lines.append("  depth: %.1f GB/s of its minimum bytes (%.4g B: depth K/V in, their gradients out, "
+                     "q and dout in, fp32 dq share out)" % (b_depth / stats["moda_bwd depth"][1] / 1e6, b_depth))
+    lines += ["", "  (the rows and depth kernels run only in the L=48 call; dq and dkv in both, so their",
+              "   averages mix the L=48 and L=0 calls, which differ only in the depth share dq adds)", "",
+              "HBM traffic per launch (FETCH_SIZE / WRITE_SIZE passes, calibrated on the depth packer:",
+              "FETCH_SIZE x %.4f, WRITE_SIZE x %.4f):" % (f_scale, w_scale),
+              "  commands: " + command[1], "            " + command[2], ""]
+    for lab in ("moda_bwd rows", "moda_bwd depth", "moda_bwd dq", "moda_bwd dkv"):
+        rd = counters["FETCH_SIZE"].get(lab, 0.0) * f_scale
+        wr = counters["WRITE_SIZE"].get(lab, 0.0) * w_scale
+        lines.append("  %-22s read %.4g B  write %.4g B" % (lab, rd, wr))
+    with open(os.path.join(os.path.dirname(TRAFFIC_FILE), "moda_bwd_long_L48.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -212,6 +256,8 @@ def summarize(trace_dir, fetch_dir, write_dir, command, sq_dir=None):
         f.write("\n".join(lines) + "\n")
     if "moda_decode partial" in stats and "moda_decode merge" in stats:
         _decode_summary(stats, counters, f_scale, w_scale, command)
+    if "moda_bwd dkv" in stats:
+        _bwd_summary(stats, counters, f_scale, w_scale, command)
     with open(TRAFFIC_FILE, "w") as f:
         json.dump({"kernel": "moda_fwd_bf16 L=48", "kernel_source_hash": kernel_source_hash(),
                    "hbm_bytes_per_launch": traffic["moda_fwd_bf16 L=48"],
@@ -256,6 +302,50 @@ def decode_leg(iters=20, warmup=3):
                          "frac": round(gbs / PEAK_HBM_GBS, 4)}}
 
 
+def backward_leg(shape, dev, kd, vd, out, lse, out0, lse0, iters=4):
+    """The backward of the long-context layer (L=48, and L=0 for the ratio) for the forward's
+    saved (out, lse), timed with HIP events on the current stream after one warm-up call;
+    inputs and the output gradient resident in HBM, L=48 and L=0 calls interleaved."""
+    shape0 = I.workload(5, 1)
+    dout = I.random_dout(shape, 7005, device="cuda")
+    B, T, Hq, Hk, d, L = shape.B, shape.T, shape.Hq, shape.Hk, shape.d, shape.L
+    ws = torch.empty(api.moda_attn_bwd_workspace(B, T, Hq, Hk, d, L), dtype=torch.uint8, device="cuda")
+    grads = (torch.empty_like(dev["q"]), torch.empty_like(dev["k_seq"]), torch.empty_like(dev["v_seq"]),
+             torch.empty_like(kd), torch.empty_like(vd))
+    grads0 = grads[:3] + (None, None)
+    stream = torch.cuda.current_stream()
+
+    def run(depth):
+        if depth:
+            api.moda_attn_bwd(dev["q"], dev["k_seq"], dev["v_seq"], kd, vd, out, lse, dout, causal=True,
+                              grads=grads, workspace=ws)
+        else:
+            api.moda_attn_bwd(dev["q"], dev["k_seq"], dev["v_seq"], None, None, out0, lse0, dout, causal=True,
+                              grads=grads0, workspace=ws)
+
+    run(True)
+    run(False)
+    t = {True: [], False: []}
+    for _ in range(iters):
+        for depth in (True, False):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            run(depth)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t[depth].append(e0.elapsed_time(e1))
+    ms, ms0 = float(np.median(t[True])), float(np.median(t[False]))
+    F, F0 = acc.bwd_flops(shape), acc.bwd_flops(shape0)
+    tf = F / (ms * 1e-3) / 1e12
+    del dout, ws, grads, grads0
+    return {"workload": "backward of the long-context layer B=1 T=65536 Hq=16 Hk=4 d=128 L=48 causal "
+                        "(dq, dk, dv, depth dk, dv from the saved out and lse)",
+            "ms": round(ms, 3), "l0_ms": round(ms0, 3), "ratio_vs_l0": round(ms / ms0, 4),
+            "flops": F, "tflops": round(tf, 2), "l0_tflops": round(F0 / (ms0 * 1e-3) / 1e12, 2),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -264,6 +354,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
     ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write the profiles/ summary from rocprofv3 CSV output directories and exit")
     ap.add_argument("--sq", metavar="SQ_DIR", nargs="+", help="with --summarize: also summarise SQ counter passes")
@@ -352,6 +443,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
     }
+    if not args.no_backward:
+        rec["backward"] = backward_leg(shape, dev, kd, vd, out, lse, out0, lse0)
     if not args.no_decode:
         rec["decode"] = decode_leg()
     if not args.no_cpu_baseline:

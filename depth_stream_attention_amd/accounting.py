@@ -43,6 +43,23 @@ def algorithmic_bytes(shape) -> int:
     return q_out + kv + depth_bytes(s) + 4 * s.B * s.Hq * s.T
 
 
+def bwd_flops(shape) -> int:
+    """Algorithmic flops of the backward: five products per visible (row, candidate) pair --
+    the recomputed scores Q K^T, dP = dO V^T, dV += P^T dO, dK += dS^T Q, dQ += dS K --
+    2*d flops each, i.e. 2.5 times the forward's."""
+    s = shape
+    return 10 * s.d * s.B * s.Hq * (visible_pairs(s.T, s.causal) + s.T * s.L)
+
+
+def bwd_bytes(shape) -> int:
+    """Minimum bytes of the backward: q, out, dout read and dq written ([B,T,Hq,d]); k, v read
+    and dk, dv written ([B,T,Hk,d]); depth K/V read and their gradients written; lse read."""
+    s = shape
+    e = elem_bytes(s)
+    return (4 * s.B * s.T * s.Hq * s.d * e + 4 * s.B * s.T * s.Hk * s.d * e + 2 * depth_bytes(s)
+            + 4 * s.B * s.Hq * s.T)
+
+
 def decode_bytes(B, T, Hq, Hk, d, L, e=2) -> int:
     """Minimum bytes of one decode step: the K/V cache and the token's depth slots read
     once, q read, out written (e bytes per element), lse written (fp32)."""

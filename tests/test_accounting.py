@@ -38,3 +38,13 @@ def test_decode_bytes_and_flops():
     # 2*(2*2*3*4)*2 = 192, q and out 2*(2*8*4)*2 = 256, lse 4*(2*8) = 64.
     assert acc.decode_bytes(2, 10, 8, 2, 4, 3) == 640 + 192 + 256 + 64
     assert acc.decode_flops(2, 10, 8, 4, 3) == 4 * 4 * 2 * 8 * 13
+
+
+def test_bwd_accounting():
+    s = I.workload(5, 0)
+    P = 65536 * 65537 // 2
+    assert acc.bwd_flops(s) == 10 * 128 * 16 * (P + 65536 * 48)
+    assert acc.bwd_flops(s) * 2 == 5 * acc.flops(s)  # 2.5 x the forward
+    e = 2
+    assert acc.bwd_bytes(s) == (4 * 65536 * 16 * 128 * e + 4 * 65536 * 4 * 128 * e
+                                + 4 * 65536 * 4 * 48 * 128 * e + 4 * 16 * 65536)
