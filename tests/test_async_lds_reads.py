@@ -37,11 +37,21 @@ def scan(asm_text):
         if t.startswith(";;#ASMEND"):
             in_asm = False
             continue
-        if not t or t.startswith(";") or t.startswith(".") or t.endswith(":"):
-            if t.endswith(":") and not t.startswith("."):
-                pending.clear()  # a function label: a new kernel starts
+        if not t or t.startswith(";") or (t.startswith(".") and not t.endswith(":")):
+            continue
+        if t.endswith(":"):
+            # A label: control may arrive from elsewhere.  Every async read must
+            # have been waited for within its own basic block.
+            if pending and t.startswith("."):
+                bad.append("line %d: label %s reached with async reads pending (%s)" % (ln, t, sorted(pending)[:4]))
+            pending.clear()
             continue
         parts = t.replace(",", " ").split()
+        if parts[0].startswith("s_branch") or parts[0].startswith("s_cbranch"):
+            if pending:
+                bad.append("line %d: branch with async reads pending (%s)" % (ln, sorted(pending)[:4]))
+            pending.clear()
+            continue
         if in_asm and parts[0] == "ds_read_b64_tr_b16":
             n += 1
             for r in _regs(parts[1]):
@@ -68,6 +78,13 @@ def test_no_use_before_wait(tmp_path):
     n, bad = scan(out.read_text())
     assert n > 0, "no inline-asm transposed reads found: the check is looking at the wrong code"
     assert not bad, "\n".join(bad[:10])
+
+
+def test_scanner_flags_pending_reads_across_control_flow():
+    text = "\n".join(["kern:", ";;#ASMSTART", "ds_read_b64_tr_b16 v[4:5], v1", ";;#ASMEND",
+                      "s_cbranch_scc1 .LBB0_2", "s_waitcnt lgkmcnt(0)", ".LBB0_2:", "v_mov_b32 v10, v4"])
+    n, bad = scan(text)
+    assert n == 1 and len(bad) == 1 and "branch" in bad[0]
 
 
 def test_scanner_flags_an_early_use():
