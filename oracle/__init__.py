@@ -9,6 +9,7 @@ from .oracle import (  # noqa: F401
     moda_fwd_rows,
     moda_bwd,
     moda_bwd_sampled,
+    kv_project,
     pack_depth,
     append_depth_slot,
     default_threads,

@@ -611,6 +611,32 @@ int moda_oracle_bwd_sampled(const void* q, const void* k_seq, const void* v_seq,
   return failed ? -5 : 0;
 }
 
+/* ---- depth write: KV projection ------------------------------------------------
+ *
+ * A layer's depth KV comes from the attention branch (its own K, V) or from a KV
+ * projection of the FFN input ([Notes] 二.3).  Either is a projection of a
+ * token's hidden state x [Dm] by a fused weight w [2*Hk*d][Dm] (output channel n
+ * = row n: K channels first, then V), by definition
+ *   k[b,t,hk,c] = sum_m x[b,t,m] * w[hk*d + c][m]
+ *   v[b,t,hk,c] = sum_m x[b,t,m] * w[Hk*d + hk*d + c][m]
+ * Outputs fp64 [B][T][Hk][d]. */
+int moda_oracle_kv_project(const void* x, const void* w, int kind, int B, int T, int Dm, int Hk, int d, double* k_out,
+                           double* v_out) {
+  if (!x || !w || !k_out || !v_out) return -1;
+  if (B <= 0 || T <= 0 || Dm <= 0 || Hk <= 0 || d <= 0) return -2;
+  if (kind < ORC_F64 || kind > ORC_BF16) return -3;
+  const int N = Hk * d;
+  for (long long bt = 0; bt < (long long)B * T; ++bt)
+    for (int n = 0; n < 2 * N; ++n) {
+      double acc = 0.0;
+      for (int m = 0; m < Dm; ++m)
+        acc += orc_load(x, (size_t)bt * Dm + m, kind) * orc_load(w, (size_t)n * Dm + m, kind);
+      double* dst = n < N ? k_out : v_out;
+      dst[(size_t)bt * N + (n % N)] = acc;
+    }
+  return 0;
+}
+
 /* Depth-stream packing, by definition: dst[b][t][hk][l][:] = src[b][t][l][hk][:]
  * for elements of elem_bytes bytes.  This is the reorganisation that keeps
  * each position's L depth states together ([Summ] 3.2), with the KV head

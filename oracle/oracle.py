@@ -37,6 +37,8 @@ def _load():
         lib.moda_oracle_bwd_sampled.argtypes = ([vp] * 6 + [i32] * 8 + [vp, i64, vp, vp, i64, vp, vp, vp, i64, vp, vp]
                                                 + [i32])
         lib.moda_oracle_bwd_sampled.restype = i32
+        lib.moda_oracle_kv_project.argtypes = [vp, vp] + [i32] * 6 + [vp, vp]
+        lib.moda_oracle_kv_project.restype = i32
         lib.moda_oracle_pack_depth.argtypes = [vp, vp] + [i32] * 6
         lib.moda_oracle_pack_depth.restype = i32
         lib.moda_oracle_append_depth_slot.argtypes = [vp, vp] + [i32] * 7
@@ -182,6 +184,25 @@ def moda_bwd_sampled(q, k_seq, v_seq, k_depth, v_depth, dout, rows=(), keys=(), 
     if rc != 0:
         raise RuntimeError("moda_oracle_bwd_sampled failed with code %d" % rc)
     return dq, dk, dv, dkd, dvd
+
+
+def kv_project(x, w_kv, Hk, d):
+    """k, v = the KV projection of x [B,T,Dm] by w_kv [2*Hk*d, Dm] (K rows, then V rows), in
+    fp64: returns (k, v) [B,T,Hk,d]."""
+    lib = _load()
+    xa, kind = _host(x)
+    wa, wkind = _host(w_kv)
+    if kind != wkind:
+        raise TypeError("x and w_kv must share one dtype")
+    B, T, Dm = xa.shape
+    if wa.shape != (2 * Hk * d, Dm):
+        raise ValueError("w_kv must be [2*Hk*d, Dm]")
+    k = np.empty((B, T, Hk, d))
+    v = np.empty((B, T, Hk, d))
+    rc = lib.moda_oracle_kv_project(_ptr(xa), _ptr(wa), kind, B, T, Dm, Hk, d, _ptr(k), _ptr(v))
+    if rc != 0:
+        raise RuntimeError("moda_oracle_kv_project failed with code %d" % rc)
+    return k, v
 
 
 def _raw_bytes(x):

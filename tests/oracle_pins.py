@@ -342,3 +342,28 @@ def pin_bwd_sampled(seed, causal=True, tol=1e-11):
         assert np.abs(dkd[i] - wkd[b, t, :, hk]).max() <= tol, "sampled depth dk differs from autograd"
         assert np.abs(dvd[i] - wvd[b, t, :, hk]).max() <= tol, "sampled depth dv differs from autograd"
     assert G == 2
+
+
+# ---- depth write: KV projection ---------------------------------------------------
+
+def pin_kv_project(seed):
+    """The projection equals numpy's matmul x @ w.T (a library routine) split into K and V
+    halves and heads; a one-hot weight selects input features; it is linear in x."""
+    g = np.random.default_rng(seed)
+    B, T, Dm, Hk, d = 2, 5, 24, 3, 4
+    x = g.standard_normal((B, T, Dm))
+    w = g.standard_normal((2 * Hk * d, Dm))
+    k, v = oracle.kv_project(x, w, Hk, d)
+    full = x @ w.T                                            # [B,T,2*Hk*d]
+    assert np.abs(k - full[..., :Hk * d].reshape(B, T, Hk, d)).max() <= 1e-12, "K half differs from x @ w.T"
+    assert np.abs(v - full[..., Hk * d:].reshape(B, T, Hk, d)).max() <= 1e-12, "V half differs from x @ w.T"
+    sel = np.zeros_like(w)
+    for n in range(2 * Hk * d):
+        sel[n, (3 * n + 1) % Dm] = 1.0
+    ks, vs = oracle.kv_project(x, sel, Hk, d)
+    idx = [(3 * n + 1) % Dm for n in range(2 * Hk * d)]
+    assert np.array_equal(ks.reshape(B, T, -1), x[..., idx[:Hk * d]]), "one-hot K weight must select features"
+    assert np.array_equal(vs.reshape(B, T, -1), x[..., idx[Hk * d:]]), "one-hot V weight must select features"
+    k2, v2 = oracle.kv_project(2.0 * x + 1.0, w, Hk, d)
+    k1, v1 = oracle.kv_project(np.ones_like(x), w, Hk, d)
+    assert np.abs(k2 - (2 * k + k1)).max() <= 1e-12 and np.abs(v2 - (2 * v + v1)).max() <= 1e-12

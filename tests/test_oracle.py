@@ -184,3 +184,16 @@ def test_bwd_sampled_equals_full_oracle():
     for i, (b, t, hk) in enumerate(toks):
         assert np.abs(dkd[i] - full[3][b, t, :, hk]).max() <= 1e-13
         assert np.abs(dvd[i] - full[4][b, t, :, hk]).max() <= 1e-13
+
+
+def test_kv_project_pins():
+    pins.pin_kv_project(370)
+
+
+def test_kv_project_bf16_widened_exactly():
+    g = torch.Generator("cpu").manual_seed(371)
+    x = torch.randn(1, 3, 16, generator=g).to(torch.bfloat16)
+    w = torch.randn(16, 16, generator=g).to(torch.bfloat16)
+    a = oracle.kv_project(x, w, 2, 4)
+    b = oracle.kv_project(x.double(), w.double(), 2, 4)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])

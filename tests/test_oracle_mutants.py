@@ -46,6 +46,8 @@ MUTANTS = {
                                  "j->dvd[(i * L + l) * d + c] += P[nseq + l - (l > 0)] * dorow[c];"),
     "sampled_missing_row_correction": ("for (int n = 0; n < ncand; ++n) dS_out[n] = P_out[n] * (dS_out[n] - D);",
                                        "for (int n = 0; n < ncand; ++n) dS_out[n] = P_out[n] * dS_out[n];"),
+    "kv_weight_transposed": ("orc_load(w, (size_t)n * Dm + m, kind)", "orc_load(w, (size_t)m * 2 * N + n, kind)"),
+    "kv_halves_swapped": ("double* dst = n < N ? k_out : v_out;", "double* dst = n < N ? v_out : k_out;"),
 }
 
 ALL_PINS = [
@@ -65,6 +67,7 @@ ALL_PINS = [
     lambda: pins.pin_bwd_invariants(113),
     lambda: pins.pin_bwd_sampled(114),
     lambda: pins.pin_bwd_sampled(115, causal=False),
+    lambda: pins.pin_kv_project(116),
 ]
 
 
@@ -85,7 +88,7 @@ def test_pins_reject_planted_mistake(tmp_path, monkeypatch, name):
     good = orc._load()
     mutant = ctypes.CDLL(_build_mutant(tmp_path, name))
     for fn in ("moda_oracle_fwd", "moda_oracle_fwd_rows", "moda_oracle_bwd", "moda_oracle_bwd_sampled",
-               "moda_oracle_pack_depth", "moda_oracle_append_depth_slot"):
+               "moda_oracle_kv_project", "moda_oracle_pack_depth", "moda_oracle_append_depth_slot"):
         getattr(mutant, fn).argtypes = getattr(good, fn).argtypes
         getattr(mutant, fn).restype = getattr(good, fn).restype
     monkeypatch.setattr(orc, "_lib", mutant)
