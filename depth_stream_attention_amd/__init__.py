@@ -12,5 +12,6 @@ from .api import (  # noqa: F401
     moda_attn_fwd_f32,
     moda_block_span,
     moda_error_string,
+    moda_kv_project,
     moda_pack_depth,
 )

@@ -44,6 +44,8 @@ def load():
     lib.moda_attn_bwd_workspace.restype = ctypes.c_size_t
     lib.moda_attn_decode_workspace.argtypes = [i32] * 6
     lib.moda_attn_decode_workspace.restype = ctypes.c_size_t
+    lib.moda_kv_project.argtypes = [vp, vp] + [i32] * 5 + [vp] * 4 + [i32, i32, vp]
+    lib.moda_kv_project.restype = i32
     lib.moda_pack_depth.argtypes = [vp, vp] + [i32] * 6 + [vp]
     lib.moda_pack_depth.restype = i32
     lib.moda_append_depth_slot.argtypes = [vp, vp] + [i32] * 7 + [vp]

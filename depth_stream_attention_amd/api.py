@@ -235,6 +235,39 @@ def moda_attn_decode(q, k_cache, v_cache, k_depth=None, v_depth=None, out=None, 
     return out, lse
 
 
+def moda_kv_project(x, w_kv, Hk, d, k_out=None, v_out=None, k_depth=None, v_depth=None, slot=0, stream=None):
+    """KV projection of x [B,T,Dm] by w_kv [2*Hk*d, Dm] (K rows, then V rows), bf16.  Writes the
+    result into k_out, v_out [B,T,Hk,d] and/or slot `slot` of the packed depth buffers k_depth,
+    v_depth [B,T,Hk,S,d]; with neither given, allocates and returns (k_out, v_out).  Returns
+    (k_out, v_out, k_depth, v_depth)."""
+    dtype = torch.bfloat16
+    _check(x, "x", dtype, 3)
+    _check(w_kv, "w_kv", dtype, 2)
+    B, T, Dm = x.shape
+    if tuple(w_kv.shape) != (2 * Hk * d, Dm):
+        raise ValueError("w_kv must be [2*Hk*d, Dm] = %s" % ((2 * Hk * d, Dm),))
+    if k_out is None and k_depth is None:
+        k_out = torch.empty((B, T, Hk, d), dtype=dtype, device=x.device)
+        v_out = torch.empty_like(k_out)
+    S = 0
+    if k_out is not None:
+        for t, n in ((k_out, "k_out"), (v_out, "v_out")):
+            _check(t, n, dtype, 4)
+            if tuple(t.shape) != (B, T, Hk, d):
+                raise ValueError("%s must be [B,T,Hk,d]" % n)
+    if k_depth is not None:
+        for t, n in ((k_depth, "k_depth"), (v_depth, "v_depth")):
+            _check(t, n, dtype, 5)
+        S = k_depth.shape[3]
+        if tuple(k_depth.shape) != (B, T, Hk, S, d) or tuple(v_depth.shape) != (B, T, Hk, S, d):
+            raise ValueError("depth buffers must be [B,T,Hk,S,d]")
+    rc = _lib.load().moda_kv_project(_ptr(x), _ptr(w_kv), B, T, Dm, Hk, d, _ptr(k_out), _ptr(v_out),
+                                     _ptr(k_depth), _ptr(v_depth), S, int(slot), _stream(stream))
+    if rc != MODA_OK:
+        raise MODAError("moda_kv_project", rc)
+    return k_out, v_out, k_depth, v_depth
+
+
 def _layout_check(t, name):
     if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
         raise ValueError("%s must be a contiguous GPU tensor" % name)

@@ -11,7 +11,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoda.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["moda_api.cpp", "moda_fwd_bf16.hip", "moda_fwd_f32.hip", "moda_pack.hip", "moda_decode.hip",
-           "moda_bwd.hip"]
+           "moda_bwd.hip", "moda_kvproj.hip"]
 
 # Per-source extra flags.  The bf16 kernels never produce NaN from finite
 # inputs, and without NaN semantics each fmaxf in their row-max chains needs no

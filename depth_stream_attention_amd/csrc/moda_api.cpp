@@ -89,6 +89,24 @@ int validate_bwd(const void* q, const void* k, const void* v, const void* kd, co
   return MODA_OK;
 }
 
+int validate_kv_project(const void* x, const void* w, int B, int T, int Dm, int Hk, int d, const void* k_out,
+                        const void* v_out, const void* k_depth, const void* v_depth, int S, int slot) {
+  if (!x || !w) return MODA_ERR_NULL;
+  const bool seq = k_out || v_out, depth = k_depth || v_depth;
+  if (!seq && !depth) return MODA_ERR_NULL;               // nothing to write
+  if ((seq && (!k_out || !v_out)) || (depth && (!k_depth || !v_depth))) return MODA_ERR_NULL;
+  if (B <= 0 || T <= 0 || Dm <= 0 || Hk <= 0 || d <= 0) return MODA_ERR_SHAPE;
+  if (depth && (S <= 0 || slot < 0 || slot >= S)) return MODA_ERR_SHAPE;
+  if (d != 64 && d != 128) return MODA_ERR_UNSUPPORTED;
+  if (Dm % 64 != 0) return MODA_ERR_UNSUPPORTED;        // whole 64-element chunks of the hidden size
+  if (static_cast<int64_t>(128) * Dm * 2 >= (int64_t{1} << 31)) return MODA_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(B) * T > INT_MAX / 2 || moda::kv_project_grid_blocks(B, T, Hk, d) > INT_MAX)
+    return MODA_ERR_UNSUPPORTED;
+  for (const void* p : {x, w, k_out, v_out, k_depth, v_depth})
+    if (p && !aligned16(p)) return MODA_ERR_ALIGN;
+  return MODA_OK;
+}
+
 int validate_layout(const void* src, const void* dst, int B, int T, int L, int Hk, int d, int elem_bytes) {
   if (!src || !dst) return MODA_ERR_NULL;
   if (B <= 0 || T <= 0 || L <= 0 || Hk <= 0 || d <= 0) return MODA_ERR_SHAPE;
@@ -174,6 +192,14 @@ size_t moda_attn_bwd_workspace(int B, int T, int Hq, int Hk, int d, int L) {
   if (B <= 0 || T <= 0 || Hq <= 0 || Hk <= 0 || d <= 0 || L < 0) return 0;
   if (Hq % Hk != 0) return 0;
   return moda::bwd_workspace_bytes(B, T, Hq, d, L);
+}
+
+int moda_kv_project(const void* x, const void* w_kv, int B, int T, int Dm, int Hk, int d, void* k_out, void* v_out,
+                    void* k_depth, void* v_depth, int S, int slot, moda_stream_t stream) {
+  const int rc = validate_kv_project(x, w_kv, B, T, Dm, Hk, d, k_out, v_out, k_depth, v_depth, S, slot);
+  if (rc != MODA_OK) return rc;
+  moda::KvProjArgs a{x, w_kv, B, T, Dm, Hk, d, k_out, v_out, k_depth, v_depth, S, slot, stream};
+  return moda::launch_kv_project(a) == hipSuccess ? MODA_OK : MODA_ERR_HIP;
 }
 
 size_t moda_attn_decode_workspace(int B, int T, int Hq, int Hk, int d, int L) {

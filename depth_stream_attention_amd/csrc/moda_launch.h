@@ -36,6 +36,15 @@ struct BwdArgs {
   void* stream;
 };
 
+struct KvProjArgs {
+  const void *x, *w;        // x [B*T][Dm]; w [2*Hk*d][Dm] (K rows, then V rows)
+  int B, T, Dm, Hk, d;
+  void *k_out, *v_out;      // [B*T][Hk][d] or both NULL
+  void *k_depth, *v_depth;  // packed [B*T][Hk][S][d] or both NULL
+  int S, slot;
+  void* stream;
+};
+
 hipError_t launch_fwd_bf16(const FwdArgs& a);
 hipError_t launch_fwd_f32(const FwdArgs& a);
 int64_t fwd_bf16_grid_blocks(int B, int T, int Hq, int Hk);
@@ -48,6 +57,9 @@ int64_t decode_grid_blocks(int B, int T, int Hk, int L);
 hipError_t launch_bwd_bf16(const BwdArgs& a);
 size_t bwd_workspace_bytes(int B, int T, int Hq, int d, int L);
 int64_t bwd_grid_blocks(int B, int T, int Hq, int Hk);
+
+hipError_t launch_kv_project(const KvProjArgs& a);
+int64_t kv_project_grid_blocks(int B, int T, int Hk, int d);
 
 hipError_t launch_pack_depth(const void* src, void* dst, int B, int T, int L, int Hk, int d, int elem_bytes,
                              void* stream);

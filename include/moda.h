@@ -218,6 +218,38 @@ int moda_attn_bwd(const void* q, const void* k_seq, const void* v_seq, const voi
 size_t moda_attn_bwd_workspace(int B, int T, int Hq, int Hk, int d, int L);
 
 /*
+ * Depth write path: the KV projection of a layer's hidden states, stored by the
+ * product's epilogue directly into one slot of the packed depth stream.  A
+ * layer adds to every token's depth stream its attention branch's own K, V and
+ * a KV projection of its FFN input ([Notes] 二.3; [Summ] 2.2, the write step);
+ * both are this product:
+ *   k[b,t,hk,c] = sum_m x[b,t,m] * w_kv[hk*d + c][m]
+ *   v[b,t,hk,c] = sum_m x[b,t,m] * w_kv[Hk*d + hk*d + c][m]
+ * fp32 accumulation, rounded once to bf16 (RNE); every destination receives
+ * the same bf16 values.
+ *
+ * Arguments
+ *   x        [B][T][Dm] bf16 hidden states.
+ *   w_kv     [2*Hk*d][Dm] bf16: output channels as rows (the torch Linear
+ *            layout), K channels first, then V channels.
+ *   k_out, v_out      [B][T][Hk][d] bf16 (written), or both NULL: the layer's
+ *            sequence K/V (attention branch).
+ *   k_depth, v_depth  [B][T][Hk][S][d] bf16 packed depth stream, or both NULL;
+ *            only slot `slot` of every (token, KV head) is written, the other
+ *            S - 1 slots are left untouched.
+ *   S, slot  slots per (token, KV head) in the depth buffers, 0 <= slot < S.
+ * At least one destination pair must be given.  Destinations must not alias x
+ * or w_kv.  Enqueued on `stream`; nothing is allocated or synchronised.
+ *
+ * Errors: MODA_ERR_NULL (x or w_kv NULL, no destination pair, or half a pair);
+ * MODA_ERR_SHAPE (a size <= 0; with depth buffers S <= 0 or slot outside
+ * [0, S)); MODA_ERR_UNSUPPORTED (d not 64 or 128; Dm not a multiple of 64;
+ * 128 * Dm * 2 bytes or the grid beyond 2^31); MODA_ERR_ALIGN; MODA_ERR_HIP.
+ */
+int moda_kv_project(const void* x, const void* w_kv, int B, int T, int Dm, int Hk, int d, void* k_out, void* v_out,
+                    void* k_depth, void* v_depth, int S, int slot, moda_stream_t stream);
+
+/*
  * Depth-stream pack: dst[b][t][hk][l][:] = src[b][t][l][hk][:], bit for bit.
  *
  * [Summ] 3.2 stores a position's L depth states contiguously; this layout

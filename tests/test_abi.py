@@ -181,3 +181,22 @@ def test_bwd_validation(lib):
         assert bwd(lib, **kw) == api.MODA_ERR_UNSUPPORTED, kw
     for name in ("q", "k", "v", "kd", "vd", "out", "lse", "do", "dq", "dk", "dv", "dkd", "dvd", "ws"):
         assert bwd(lib, **{name: MIS}) == api.MODA_ERR_ALIGN, name
+
+
+def kvp(lib, x=A, w=A, B=2, T=100, Dm=256, Hk=2, d=128, ko=A, vo=A, kd=A, vd=A, S=4, slot=1):
+    return lib.moda_kv_project(x, w, B, T, Dm, Hk, d, ko, vo, kd, vd, S, slot, None)
+
+
+def test_kv_project_validation(lib):
+    null = ctypes.c_void_p(0)
+    for kw in (dict(x=null), dict(w=null), dict(ko=null, vo=null, kd=null, vd=null), dict(ko=null),
+               dict(vd=null)):
+        assert kvp(lib, **kw) == api.MODA_ERR_NULL, kw
+    for kw in (dict(B=0), dict(T=0), dict(Dm=0), dict(Hk=0), dict(d=0), dict(slot=4), dict(slot=-1), dict(S=0)):
+        assert kvp(lib, **kw) == api.MODA_ERR_SHAPE, kw
+    # without depth buffers S and slot are not looked at
+    assert kvp(lib, kd=null, vd=null, slot=9, x=MIS) == api.MODA_ERR_ALIGN
+    for kw in (dict(d=96), dict(Dm=96), dict(Dm=1 << 23)):
+        assert kvp(lib, **kw) == api.MODA_ERR_UNSUPPORTED, kw
+    for name in ("x", "w", "ko", "vo", "kd", "vd"):
+        assert kvp(lib, **{name: MIS}) == api.MODA_ERR_ALIGN, name
