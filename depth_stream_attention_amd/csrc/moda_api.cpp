@@ -99,7 +99,7 @@ int validate_kv_project(const void* x, const void* w, int B, int T, int Dm, int 
   if (depth && (S <= 0 || slot < 0 || slot >= S)) return MODA_ERR_SHAPE;
   if (d != 64 && d != 128) return MODA_ERR_UNSUPPORTED;
   if (Dm % 64 != 0) return MODA_ERR_UNSUPPORTED;        // whole 64-element chunks of the hidden size
-  if (static_cast<int64_t>(128) * Dm * 2 >= (int64_t{1} << 31)) return MODA_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(256) * Dm * 2 >= (int64_t{1} << 31)) return MODA_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(B) * T > INT_MAX / 2 || moda::kv_project_grid_blocks(B, T, Hk, d) > INT_MAX)
     return MODA_ERR_UNSUPPORTED;
   for (const void* p : {x, w, k_out, v_out, k_depth, v_depth})

@@ -11,32 +11,37 @@
 // [B,T,Hk,S,d] stream afterwards, the epilogue stores each result once into
 // the slot (and, when asked, also into the layer's sequence K/V buffers).
 //
-// Decomposition: a workgroup owns 128 channels x 128 tokens, 4 waves each 64
-// channels x 64 tokens = 2 x 2 blocks of 32x32 on v_mfma_f32_32x32x16_bf16.
-// The products are formed transposed, C^T = W X^T (A = weight rows, B = token
-// rows), so that each lane owns one token and four consecutive channels per
-// register group: the epilogue stores 8 bytes per lane per group.  Dm is
-// walked in 64-element chunks, double-buffered in LDS by direct-to-LDS buffer
-// loads (16 bytes per lane, rows XOR-swizzled so the operand reads are free of
-// bank conflicts); the chunk offset is the scalar offset of the loads, so the
-// per-lane offsets are loop invariant.
+// Decomposition: a workgroup of 8 waves (two per SIMD) owns 256 channels x 256
+// tokens; wave w computes channels 128*(w%2) .. +128 x tokens 64*(w/2) .. +64 as
+// 4 x 2 blocks of 32x32 on v_mfma_f32_32x32x16_bf16 (six operand reads per
+// eight products).  The products are formed transposed, C^T = W X^T (A = weight
+// rows, B = token rows).  Dm is walked in 64-element chunks, double-buffered in
+// LDS by direct-to-LDS buffer loads (16 bytes per lane, rows XOR-swizzled so
+// the operand reads are free of bank conflicts); the chunk offset is the
+// loads' scalar offset, so the per-lane offsets are loop invariant.  The
+// epilogue rounds to bf16 and stages the 256 x 256 tile through LDS as
+// [token][channel] rows, so that each 16-byte global store holds 8 consecutive
+// channels of one token and a wave stores whole 512-byte token rows.
 #include "moda_launch.h"
 #include "moda_tile.h"
 
 namespace moda {
 namespace {
 
-constexpr int kKW = 4;                 // waves
+constexpr int kKW = 8;                 // waves
 constexpr int kKThreads = kKW * 64;
-constexpr int kTileRows = 128;         // channels and tokens per workgroup
+constexpr int kTileRows = 256;         // channels and tokens per workgroup
 constexpr int kKC = 64;                // Dm elements per LDS chunk
-constexpr int kRowBytes = kKC * 2;     // 128 bytes per tile row
-constexpr int kTileBytes = kTileRows * kRowBytes;  // 16 KiB per operand tile
+constexpr int kRowBytes = kKC * 2;     // 128 bytes per operand tile row
+constexpr int kTileBytes = kTileRows * kRowBytes;  // 32 KiB per operand tile
 constexpr int kStageBytes = 2 * kTileBytes;        // weight tile, then token tile
 constexpr int kLoadsPerWave = kTileBytes / 1024 / kKW;  // 1 KiB per wave-wide load
+constexpr int kEpiRow = kTileRows * 2 + 16;        // staged output row: 256 channels + 16 bytes of skew
+constexpr int kSmemBytes = (2 * kStageBytes > kTileRows * kEpiRow) ? 2 * kStageBytes : kTileRows * kEpiRow;
 
 // Two tile rows share one 256-byte LDS line; 16 consecutive rows read with one
-// logical chunk meet 8 distinct swizzles in each half of the line.
+// logical chunk meet 8 distinct swizzles in each half of the line.  The
+// swizzle repeats every 16 rows, so 32-row steps are immediate offsets.
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
 template <bool SEQ, bool DEPTH>
@@ -44,22 +49,29 @@ __global__ __launch_bounds__(kKThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int M, int Dm, int Hk, int d, int S, int slot,
     int n_tiles_c, uint16_t* __restrict__ k_out, uint16_t* __restrict__ v_out, uint16_t* __restrict__ k_depth,
     uint16_t* __restrict__ v_depth) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[2 * kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[kSmemBytes];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5;
-  // Channel tiles vary fastest, so consecutive workgroups share their tokens.
-  const int ct = blockIdx.x % n_tiles_c;
-  const int mt = blockIdx.x / n_tiles_c;
+  const int HD = Hk * d;
+  const int N = 2 * HD;
+  // Workgroups are dealt round-robin to the 8 XCDs (each with its own L2), so
+  // the channel tiles of one token tile are given workgroup ids that are equal
+  // mod 8: they run on one XCD and read the token tile from HBM once.
+  const int ct = (blockIdx.x / 8) % n_tiles_c;
+  const int mt = (blockIdx.x / (8 * n_tiles_c)) * 8 + blockIdx.x % 8;
+  if (mt * kTileRows >= M) return;  // padding workgroup of the last group of 8 token tiles
   const int n0 = ct * kTileRows;
   const int m0 = mt * kTileRows;
-  const int cw0 = (wave & 1) * 64;   // the wave's channels within the tile
+  const int cw0 = (wave & 1) * 128;  // the wave's channels within the tile
   const int tw0 = (wave >> 1) * 64;  // the wave's tokens within the tile
 
-  // Buffer descriptors: weight rows n0.., token rows m0.. (rows past M read as zero).
+  // Buffer descriptors: weight rows n0.. (rows past N read as zero), token rows m0..
+  // (rows past M read as zero).
   const uint32_t row_bytes = static_cast<uint32_t>(Dm) * 2;
   const int64_t xrange = static_cast<int64_t>(M - m0) * row_bytes;
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(w + static_cast<int64_t>(n0) * Dm, kTileRows * row_bytes);
+  const __amdgpu_buffer_rsrc_t rw =
+      make_rsrc(w + static_cast<int64_t>(n0) * Dm, static_cast<uint32_t>(min(N - n0, kTileRows)) * row_bytes);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + static_cast<int64_t>(m0) * Dm,
                                               static_cast<uint32_t>(xrange < 0x7fffffff ? xrange : 0x7fffffff));
   // Load instruction j of this wave fills tile rows pr = (wave*L + j)*8 + lane/8,
@@ -82,22 +94,20 @@ __global__ __launch_bounds__(kKThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     }
   };
 
-  // Operand read offsets: block b of the wave's rows, 16-element slice sl:
-  // row = base + 32*b + lane%32, logical chunk 2*sl + lane/32.
-  uint32_t rd_w[2][4], rd_x[2][4];
+  // Operand read offsets of 16-element slice sl for the wave's first block of
+  // rows: row = base + lane%32, logical chunk 2*sl + lane/32; block b adds 32*b rows.
+  uint32_t rd_w[4], rd_x[4];
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
-#pragma unroll
-    for (int sl = 0; sl < 4; ++sl) {
-      const int rw_row = cw0 + 32 * b + (lane & 31);
-      const int rx_row = tw0 + 32 * b + (lane & 31);
-      rd_w[b][sl] = rw_row * kRowBytes + (((2 * sl + half) ^ swz(rw_row)) * 16);
-      rd_x[b][sl] = kTileBytes + rx_row * kRowBytes + (((2 * sl + half) ^ swz(rx_row)) * 16);
-    }
+  for (int sl = 0; sl < 4; ++sl) {
+    const int rw_row = cw0 + (lane & 31);
+    const int rx_row = tw0 + (lane & 31);
+    rd_w[sl] = rw_row * kRowBytes + (((2 * sl + half) ^ swz(rw_row)) * 16);
+    rd_x[sl] = kTileBytes + rx_row * kRowBytes + (((2 * sl + half) ^ swz(rx_row)) * 16);
+  }
 
-  f32x16 acc[2][2];  // [channel block][token block]
+  f32x16 acc[4][2];  // [channel block][token block]
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
 
@@ -107,51 +117,69 @@ __global__ __launch_bounds__(kKThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     publish_tile();
     if (c + 1 < nch) dma(c + 1, (c + 1) & 1);
     const uint32_t base = lds_addr((lds_u8*)smem_raw) + opaque_s((c & 1) * kStageBytes);
+    // The operands of slice sl + 1 are read while the products of slice sl run.
+    bf16x8 f[2][6];
+    auto fetch = [&](bf16x8(&o)[6], int sl) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) o[a] = *lds_at<lds_bf16x8_t>(base + rd_w[sl] + 32 * a * kRowBytes);
+#pragma unroll
+      for (int b = 0; b < 2; ++b) o[4 + b] = *lds_at<lds_bf16x8_t>(base + rd_x[sl] + 32 * b * kRowBytes);
+    };
+    fetch(f[0], 0);
 #pragma unroll
     for (int sl = 0; sl < 4; ++sl) {
-      bf16x8 fa[2], fb[2];
+      if (sl + 1 < 4) fetch(f[(sl + 1) & 1], sl + 1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        fa[b] = *lds_at<lds_bf16x8_t>(base + rd_w[b][sl]);
-        fb[b] = *lds_at<lds_bf16x8_t>(base + rd_x[b][sl]);
-      }
+      for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) acc[a][b] = mfma32(fa[a], fb[b], acc[a][b]);
+        for (int b = 0; b < 2; ++b) acc[a][b] = mfma32(f[sl & 1][a], f[sl & 1][4 + b], acc[a][b]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
-  // Epilogue: acc[a][b] element i of this lane is channel n0 + cw0 + 32a + 8(i/4) +
-  // 4*half + i%4 of token m0 + tw0 + 32b + lane%32.  Four consecutive channels never
-  // cross a head, so each group is one 8-byte store per destination.
-  const int HD = Hk * d;
+  // Epilogue.  acc[a][b] element i of this lane is channel cw0 + 32a + 8(i/4) + 4*half
+  // + i%4 of token tw0 + 32b + lane%32 (tile coordinates).  Stage the bf16 tile as
+  // [token][channel] rows in LDS (every wave is done with the operand tiles first).
+  __syncthreads();
+  const uint32_t epi = lds_addr((lds_u8*)smem_raw);
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
-    const int tok = m0 + tw0 + 32 * b + (lane & 31);
-    if (tok >= M) continue;
+    const int tr = tw0 + 32 * b + (lane & 31);
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int ch = n0 + cw0 + 32 * a + 8 * g + 4 * half;
-        const bool is_v = ch >= HD;
-        const int r = is_v ? ch - HD : ch;
-        const int hk = r / d, cc = r - hk * d;
+        const int cc = cw0 + 32 * a + 8 * g + 4 * half;
         u32x2 val = {pack_bf16x2(acc[a][b][4 * g], acc[a][b][4 * g + 1]),
                      pack_bf16x2(acc[a][b][4 * g + 2], acc[a][b][4 * g + 3])};
-        const int64_t th = static_cast<int64_t>(tok) * Hk + hk;
-        if (SEQ) *reinterpret_cast<u32x2*>((is_v ? v_out : k_out) + th * d + cc) = val;
-        if (DEPTH) *reinterpret_cast<u32x2*>((is_v ? v_depth : k_depth) + (th * S + slot) * d + cc) = val;
+        *lds_at<__attribute__((address_space(3))) u32x2>(epi + tr * kEpiRow + cc * 2) = val;
       }
+  }
+  __syncthreads();
+  // Each thread stores 16-byte pieces (8 channels of one token); consecutive
+  // threads take consecutive pieces of a token row.  Eight consecutive channels
+  // never cross a head.
+  for (int j = threadIdx.x; j < kTileRows * (kTileRows / 8); j += kKThreads) {
+    const int tr = j / (kTileRows / 8), pc = j % (kTileRows / 8);
+    const int tok = m0 + tr, ch = n0 + 8 * pc;
+    if (tok >= M || ch >= N) continue;
+    const u32x4 val = *lds_at<__attribute__((address_space(3))) u32x4>(epi + tr * kEpiRow + pc * 16);
+    const bool is_v = ch >= HD;
+    const int r = is_v ? ch - HD : ch;
+    const int hk = r / d, cc = r - hk * d;
+    const int64_t th = static_cast<int64_t>(tok) * Hk + hk;
+    if (SEQ) *reinterpret_cast<u32x4*>((is_v ? v_out : k_out) + th * d + cc) = val;
+    if (DEPTH) *reinterpret_cast<u32x4*>((is_v ? v_depth : k_depth) + (th * S + slot) * d + cc) = val;
   }
 }
 
 template <bool SEQ, bool DEPTH>
 hipError_t launch(const KvProjArgs& a) {
   const int M = a.B * a.T;
-  const int n_tiles_c = 2 * a.Hk * a.d / kTileRows;
-  const int64_t blocks = static_cast<int64_t>((M + kTileRows - 1) / kTileRows) * n_tiles_c;
+  const int n_tiles_c = (2 * a.Hk * a.d + kTileRows - 1) / kTileRows;
+  const int64_t groups = ((M + kTileRows - 1) / kTileRows + 7) / 8;  // groups of 8 token tiles
+  const int64_t blocks = groups * 8 * n_tiles_c;
   hipLaunchKernelGGL((moda_kv_project_kernel<SEQ, DEPTH>), dim3(static_cast<unsigned>(blocks)), dim3(kKThreads), 0,
                      static_cast<hipStream_t>(a.stream), static_cast<const uint16_t*>(a.x),
                      static_cast<const uint16_t*>(a.w), M, a.Dm, a.Hk, a.d, a.S, a.slot, n_tiles_c,
@@ -164,7 +192,7 @@ hipError_t launch(const KvProjArgs& a) {
 
 int64_t kv_project_grid_blocks(int B, int T, int Hk, int d) {
   const int64_t M = static_cast<int64_t>(B) * T;
-  return (M + kTileRows - 1) / kTileRows * (2 * static_cast<int64_t>(Hk) * d / kTileRows);
+  return ((M + kTileRows - 1) / kTileRows + 7) / 8 * 8 * ((2 * static_cast<int64_t>(Hk) * d + kTileRows - 1) / kTileRows);
 }
 
 hipError_t launch_kv_project(const KvProjArgs& a) {

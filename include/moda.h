@@ -244,7 +244,7 @@ size_t moda_attn_bwd_workspace(int B, int T, int Hq, int Hk, int d, int L);
  * Errors: MODA_ERR_NULL (x or w_kv NULL, no destination pair, or half a pair);
  * MODA_ERR_SHAPE (a size <= 0; with depth buffers S <= 0 or slot outside
  * [0, S)); MODA_ERR_UNSUPPORTED (d not 64 or 128; Dm not a multiple of 64;
- * 128 * Dm * 2 bytes or the grid beyond 2^31); MODA_ERR_ALIGN; MODA_ERR_HIP.
+ * 256 * Dm * 2 bytes or the grid beyond 2^31); MODA_ERR_ALIGN; MODA_ERR_HIP.
  */
 int moda_kv_project(const void* x, const void* w_kv, int B, int T, int Dm, int Hk, int d, void* k_out, void* v_out,
                     void* k_depth, void* v_depth, int S, int slot, moda_stream_t stream);
