@@ -105,6 +105,8 @@ def _kernel_label(name):
     for k in ("rows", "depth", "dq", "dkv"):
         if "moda_bwd_%s_kernel" % k in name:
             return "moda_bwd %s" % k
+    if "moda_kv_project_kernel" in name:
+        return "moda_kv_project"
     return None
 
 
@@ -202,6 +204,31 @@ def _bwd_summary(stats, counters, f_scale, w_scale, command):
     print("\n".join(lines))
 
 
+def _kvproj_summary(stats, counters, f_scale, w_scale, command):
+    """profiles/moda_kv_project_long.txt: the depth-write KV projection of the same bench run."""
+    s = KVPROJ_SHAPE
+    F = acc.kv_project_flops(s["B"], s["T"], s["Dm"], s["Hk"], s["d"])
+    byts = acc.kv_project_bytes(s["B"], s["T"], s["Dm"], s["Hk"], s["d"])
+    n, avg, mn, mx = stats["moda_kv_project"]
+    rd = counters["FETCH_SIZE"].get("moda_kv_project", 0.0) * f_scale
+    wr = counters["WRITE_SIZE"].get("moda_kv_project", 0.0) * w_scale
+    lines = ["# rocprofv3 summary: depth write (KV projection into the sequence K/V and one packed depth slot),",
+             "# B=%d T=%d Dm=%d Hk=%d d=%d, bf16" % (s["B"], s["T"], s["Dm"], s["Hk"], s["d"]), "",
+             "kernel trace (rocprofv3 --kernel-trace --stats):", "  command: " + command[0], "",
+             "  %-22s %6s %12s %12s %12s" % ("kernel", "calls", "avg ms", "min ms", "max ms"),
+             "  %-22s %6d %12.4f %12.4f %12.4f" % ("moda_kv_project", n, avg, mn, mx), "",
+             "  %.1f TFLOP/s (%.4g flop; %.1f%% of the 2.5 PFLOP/s bf16 peak)" % (F / avg / 1e9, F,
+                                                                                 F / avg / 1e9 / PEAK_BF16_TFLOPS * 100),
+             "", "HBM traffic per launch (FETCH_SIZE / WRITE_SIZE passes, calibrated on the depth packer:",
+             "FETCH_SIZE x %.4f, WRITE_SIZE x %.4f):" % (f_scale, w_scale),
+             "  commands: " + command[1], "            " + command[2], "",
+             "  read %.4g B  write %.4g B  (minimum: %.4g B = x and w read once, every output written to both"
+             % (rd, wr, byts), "  destinations)"]
+    with open(os.path.join(os.path.dirname(TRAFFIC_FILE), "moda_kv_project_long.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def summarize(trace_dir, fetch_dir, write_dir, command, sq_dir=None):
     """Turn rocprofv3 CSVs of this benchmark into the committed summary and traffic record.
 
@@ -258,6 +285,8 @@ def summarize(trace_dir, fetch_dir, write_dir, command, sq_dir=None):
         _decode_summary(stats, counters, f_scale, w_scale, command)
     if "moda_bwd dkv" in stats:
         _bwd_summary(stats, counters, f_scale, w_scale, command)
+    if "moda_kv_project" in stats:
+        _kvproj_summary(stats, counters, f_scale, w_scale, command)
     with open(TRAFFIC_FILE, "w") as f:
         json.dump({"kernel": "moda_fwd_bf16 L=48", "kernel_source_hash": kernel_source_hash(),
                    "hbm_bytes_per_launch": traffic["moda_fwd_bf16 L=48"],
@@ -346,6 +375,45 @@ def backward_leg(shape, dev, kd, vd, out, lse, out0, lse0, iters=4):
                          "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
 
 
+KVPROJ_SHAPE = dict(B=1, T=65536, Dm=2048, Hk=4, d=128)
+
+
+def depth_write_leg(kd, vd, iters=10):
+    """The depth write path at the long-context layer: the KV projection of 65536 hidden states
+    (Dm = Hq*d = 2048) into the layer's sequence K/V and the last slot of the step's packed depth
+    buffers, one fused launch, timed with HIP events after warm-up."""
+    s = KVPROJ_SHAPE
+    B, T, Dm, Hk, d = s["B"], s["T"], s["Dm"], s["Hk"], s["d"]
+    g = torch.Generator(device="cuda").manual_seed(13)
+    x = torch.randn(B, T, Dm, device="cuda", generator=g).bfloat16()
+    w = (torch.randn(2 * Hk * d, Dm, device="cuda", generator=g) / 8).bfloat16()
+    k = torch.empty(B, T, Hk, d, dtype=torch.bfloat16, device="cuda")
+    v = torch.empty_like(k)
+    slot = kd.shape[3] - 1
+
+    def run():
+        api.moda_kv_project(x, w, Hk, d, k_out=k, v_out=v, k_depth=kd, v_depth=vd, slot=slot)
+
+    run()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(iters):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    F = acc.kv_project_flops(B, T, Dm, Hk, d)
+    tf = F / (ms * 1e-3) / 1e12
+    del x, w, k, v
+    return {"workload": "depth write: KV projection of B=1 T=65536 hidden states (Dm=2048) into the sequence "
+                        "K/V and slot %d of the packed depth stream (Hk=4 d=128), one launch" % slot,
+            "ms": round(ms, 4), "flops": F, "bytes": acc.kv_project_bytes(B, T, Dm, Hk, d),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -355,6 +423,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
+    ap.add_argument("--no-depth-write", action="store_true", help="skip the depth-write (KV projection) measurement")
     ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write the profiles/ summary from rocprofv3 CSV output directories and exit")
     ap.add_argument("--sq", metavar="SQ_DIR", nargs="+", help="with --summarize: also summarise SQ counter passes")
@@ -447,6 +516,8 @@ def main():
         rec["backward"] = backward_leg(shape, dev, kd, vd, out, lse, out0, lse0)
     if not args.no_decode:
         rec["decode"] = decode_leg()
+    if not args.no_depth_write:  # last: it overwrites the final depth slot of the step's buffers
+        rec["depth_write"] = depth_write_leg(kd, vd)
     if not args.no_cpu_baseline:
         host = {k: v.cpu() for k, v in dev.items()}
         cpu, rows, ref = cpu_baseline(shape, host, args.cpu_seconds)

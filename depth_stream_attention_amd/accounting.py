@@ -60,6 +60,17 @@ def bwd_bytes(shape) -> int:
             + 4 * s.B * s.Hq * s.T)
 
 
+def kv_project_flops(B, T, Dm, Hk, d) -> int:
+    """The depth-write KV projection: tokens x (2*Hk*d) outputs, Dm multiply-adds each."""
+    return 2 * B * T * Dm * 2 * Hk * d
+
+
+def kv_project_bytes(B, T, Dm, Hk, d, e=2) -> int:
+    """Minimum bytes of the fused KV projection writing both the sequence K/V and one depth
+    slot: x and w read once, each output element written twice."""
+    return B * T * Dm * e + 2 * Hk * d * Dm * e + 2 * (2 * B * T * Hk * d * e)
+
+
 def decode_bytes(B, T, Hq, Hk, d, L, e=2) -> int:
     """Minimum bytes of one decode step: the K/V cache and the token's depth slots read
     once, q read, out written (e bytes per element), lse written (fp32)."""

@@ -48,3 +48,9 @@ def test_bwd_accounting():
     e = 2
     assert acc.bwd_bytes(s) == (4 * 65536 * 16 * 128 * e + 4 * 65536 * 4 * 128 * e
                                 + 4 * 65536 * 4 * 48 * 128 * e + 4 * 16 * 65536)
+
+
+def test_kv_project_accounting():
+    assert acc.kv_project_flops(1, 65536, 2048, 4, 128) == 2 * 65536 * 2048 * 1024
+    assert acc.kv_project_bytes(1, 65536, 2048, 4, 128) == (65536 * 2048 * 2 + 1024 * 2048 * 2
+                                                            + 2 * 65536 * 1024 * 2)
