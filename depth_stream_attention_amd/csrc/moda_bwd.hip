@@ -616,68 +616,88 @@ __device__ __forceinline__ void load_rows(bf16x8 (&aq)[D / 16], bf16x8 (&ao)[D /
   }
 }
 
-template <int D>
-__device__ __forceinline__ bf16x8 read_tr8(const TileReads<D>& ta, int dt, int off) {
-  const s16x4 lo4 = read_tr_async(ta.lo[dt] + off);
-  const s16x4 hi4 = read_tr_async(ta.hi[dt] + off);
+// A transposed A operand (two async reads) at a compile-time byte offset, which
+// goes into the instructions' offset field instead of costing an address add.
+template <int OFF>
+__device__ __forceinline__ s16x4 read_tr_async_at(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "LDS instruction offset field");
+  s16x4 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+
+template <int D, int OFF>
+__device__ __forceinline__ bf16x8 read_tr8(const TileReads<D>& ta, int dt) {
+  const s16x4 lo4 = read_tr_async_at<OFF>(ta.lo[dt]);
+  const s16x4 hi4 = read_tr_async_at<OFF>(ta.hi[dt]);
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// 32-row block J of the tile: scores from the operands already in aq/ao (the
+// next block's are fetched meanwhile), weights, then dV^T and dK^T.
+template <int D, bool MASK, int J>
+__device__ __forceinline__ void kv_block(f32x16 (&dka)[D / 32], f32x16 (&dva)[D / 32], const bf16x8 (&kf)[D / 16],
+                                         const bf16x8 (&vf)[D / 16], bf16x8 (&aq)[D / 16], bf16x8 (&ao)[D / 16],
+                                         const TileReads<D>& qa, uint32_t stat, int r0, int lgG, int my_key,
+                                         int half, float scale_log2) {
+  using TL = Tile<D>;
+  using RS = RowStage<D>;
+  constexpr int DO = RS::DO - RS::Q;
+  constexpr int NT = D / 32;
+  f32x16 s = {}, dp = {};
+#pragma unroll
+  for (int sl = 0; sl < D / 16; ++sl) {
+    s = mfma32(aq[sl], kf[sl], s);  // [row][key]
+    dp = mfma32(ao[sl], vf[sl], dp);
+  }
+  bf16x8 tt[4 * NT];  // [h][dO, Q][dt]
+#pragma unroll
+  for (int dt = 0; dt < NT; ++dt) {
+    tt[0 * NT + dt] = read_tr8<D, (32 * J) * TL::ROW_BYTES + DO>(qa, dt);
+    tt[1 * NT + dt] = read_tr8<D, (32 * J) * TL::ROW_BYTES>(qa, dt);
+    tt[2 * NT + dt] = read_tr8<D, (32 * J + 16) * TL::ROW_BYTES + DO>(qa, dt);
+    tt[3 * NT + dt] = read_tr8<D, (32 * J + 16) * TL::ROW_BYTES>(qa, dt);
+  }
+  if (J == 0) load_rows<D>(aq, ao, qa, 32 * TL::ROW_BYTES, DO);
+  __builtin_amdgcn_sched_barrier(0);
+  float p[16], ds[16];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int rr = 32 * J + 8 * a + 4 * half;  // tile rows rr .. rr+3 in registers 4a .. 4a+3
+    const f32x4 l2 = *lds_at<lds_f32x4_t>(stat + RS::L2 + rr * 4);
+    const f32x4 dd = *lds_at<lds_f32x4_t>(stat + RS::DD + rr * 4);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int i = 4 * a + c;
+      float x = fmaf(s[i], scale_log2, -l2[c]);
+      if (MASK) x = my_key <= ((r0 + rr + c) >> lgG) ? x : -INFINITY;
+      p[i] = fast_exp2(x);
+      ds[i] = p[i] * (dp[i] - dd[c]);
+    }
+  }
+  bf16x8 pb[2], db[2];
+  pack16(p, pb);
+  pack16(ds, db);
+  lds_ready(tt);
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int dt = 0; dt < NT; ++dt) {
+      dva[dt] = mfma32(tt[(2 * h) * NT + dt], pb[h], dva[dt]);
+      dka[dt] = mfma32(tt[(2 * h + 1) * NT + dt], db[h], dka[dt]);
+    }
 }
 
 template <int D, bool MASK>
 __device__ __forceinline__ void kv_tile(f32x16 (&dka)[D / 32], f32x16 (&dva)[D / 32], const bf16x8 (&kf)[D / 16],
                                         const bf16x8 (&vf)[D / 16], const TileReads<D>& qa, uint32_t stat, int r0,
                                         int lgG, int my_key, int half, float scale_log2) {
-  using TL = Tile<D>;
-  using RS = RowStage<D>;
-  constexpr int DO = RS::DO - RS::Q;
+  constexpr int DO = RowStage<D>::DO - RowStage<D>::Q;
   bf16x8 aq[D / 16], ao[D / 16];
   load_rows<D>(aq, ao, qa, 0, DO);
   __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    f32x16 s = {}, dp = {};
-#pragma unroll
-    for (int sl = 0; sl < D / 16; ++sl) {
-      s = mfma32(aq[sl], kf[sl], s);     // [row][key]
-      dp = mfma32(ao[sl], vf[sl], dp);
-    }
-    bf16x8 tt[4 * (D / 32)];  // [h][dO, Q][dt]
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        tt[(2 * h) * (D / 32) + dt] = read_tr8<D>(qa, dt, (32 * j + 16 * h) * TL::ROW_BYTES + DO);
-        tt[(2 * h + 1) * (D / 32) + dt] = read_tr8<D>(qa, dt, (32 * j + 16 * h) * TL::ROW_BYTES);
-      }
-    if (j == 0) load_rows<D>(aq, ao, qa, 32 * TL::ROW_BYTES, DO);
-    __builtin_amdgcn_sched_barrier(0);
-    float p[16], ds[16];
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int rr = 32 * j + 8 * a + 4 * half;  // tile rows rr .. rr+3 in registers 4a .. 4a+3
-      const f32x4 l2 = *lds_at<lds_f32x4_t>(stat + RS::L2 + rr * 4);
-      const f32x4 dd = *lds_at<lds_f32x4_t>(stat + RS::DD + rr * 4);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int i = 4 * a + c;
-        float x = fmaf(s[i], scale_log2, -l2[c]);
-        if (MASK) x = my_key <= ((r0 + rr + c) >> lgG) ? x : -INFINITY;
-        p[i] = fast_exp2(x);
-        ds[i] = p[i] * (dp[i] - dd[c]);
-      }
-    }
-    bf16x8 pb[2], db[2];
-    pack16(p, pb);
-    pack16(ds, db);
-    lds_ready(tt);
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        dva[dt] = mfma32(tt[(2 * h) * (D / 32) + dt], pb[h], dva[dt]);
-        dka[dt] = mfma32(tt[(2 * h + 1) * (D / 32) + dt], db[h], dka[dt]);
-      }
-  }
+  kv_block<D, MASK, 0>(dka, dva, kf, vf, aq, ao, qa, stat, r0, lgG, my_key, half, scale_log2);
+  kv_block<D, MASK, 1>(dka, dva, kf, vf, aq, ao, qa, stat, r0, lgG, my_key, half, scale_log2);
 }
 
 template <int D, bool CAUSAL>
