@@ -633,24 +633,11 @@ __device__ __forceinline__ bf16x8 read_tr8(const TileReads<D>& ta, int dt) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// 32-row block J of the tile: scores from the operands already in aq/ao (the
-// next block's are fetched meanwhile), weights, then dV^T and dK^T.
-template <int D, bool MASK, int J>
-__device__ __forceinline__ void kv_block(f32x16 (&dka)[D / 32], f32x16 (&dva)[D / 32], const bf16x8 (&kf)[D / 16],
-                                         const bf16x8 (&vf)[D / 16], bf16x8 (&aq)[D / 16], bf16x8 (&ao)[D / 16],
-                                         const TileReads<D>& qa, uint32_t stat, int r0, int lgG, int my_key,
-                                         int half, float scale_log2) {
+template <int D, int J>
+__device__ __forceinline__ void kv_fetch_tr(bf16x8 (&tt)[4 * (D / 32)], const TileReads<D>& qa) {
   using TL = Tile<D>;
-  using RS = RowStage<D>;
-  constexpr int DO = RS::DO - RS::Q;
+  constexpr int DO = RowStage<D>::DO - RowStage<D>::Q;
   constexpr int NT = D / 32;
-  f32x16 s = {}, dp = {};
-#pragma unroll
-  for (int sl = 0; sl < D / 16; ++sl) {
-    s = mfma32(aq[sl], kf[sl], s);  // [row][key]
-    dp = mfma32(ao[sl], vf[sl], dp);
-  }
-  bf16x8 tt[4 * NT];  // [h][dO, Q][dt]
 #pragma unroll
   for (int dt = 0; dt < NT; ++dt) {
     tt[0 * NT + dt] = read_tr8<D, (32 * J) * TL::ROW_BYTES + DO>(qa, dt);
@@ -658,27 +645,56 @@ __device__ __forceinline__ void kv_block(f32x16 (&dka)[D / 32], f32x16 (&dva)[D 
     tt[2 * NT + dt] = read_tr8<D, (32 * J + 16) * TL::ROW_BYTES + DO>(qa, dt);
     tt[3 * NT + dt] = read_tr8<D, (32 * J + 16) * TL::ROW_BYTES>(qa, dt);
   }
-  if (J == 0) load_rows<D>(aq, ao, qa, 32 * TL::ROW_BYTES, DO);
-  __builtin_amdgcn_sched_barrier(0);
-  float p[16], ds[16];
+}
+
+template <int D>
+__device__ __forceinline__ void kv_scores(const bf16x8 (&aq)[D / 16], const bf16x8 (&ao)[D / 16],
+                                          const bf16x8 (&kf)[D / 16], const bf16x8 (&vf)[D / 16], f32x16& s,
+                                          f32x16& dp) {
+  s = f32x16{};
+  dp = f32x16{};
+#pragma unroll
+  for (int sl = 0; sl < D / 16; ++sl) {
+    s = mfma32(aq[sl], kf[sl], s);  // [row][key]
+    dp = mfma32(ao[sl], vf[sl], dp);
+  }
+}
+
+// lse2 and Dsum of the 16 rows of block J this lane's score registers cover.
+template <int D, int J>
+__device__ __forceinline__ void kv_stats(uint32_t stat, int half, f32x4 (&l2)[4], f32x4 (&dd)[4]) {
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
     const int rr = 32 * J + 8 * a + 4 * half;  // tile rows rr .. rr+3 in registers 4a .. 4a+3
-    const f32x4 l2 = *lds_at<lds_f32x4_t>(stat + RS::L2 + rr * 4);
-    const f32x4 dd = *lds_at<lds_f32x4_t>(stat + RS::DD + rr * 4);
+    l2[a] = *lds_at<lds_f32x4_t>(stat + RowStage<D>::L2 + rr * 4);
+    dd[a] = *lds_at<lds_f32x4_t>(stat + RowStage<D>::DD + rr * 4);
+  }
+}
+
+template <int J, bool MASK>
+__device__ __forceinline__ void kv_weights(const f32x16& s, const f32x16& dp, const f32x4 (&l2)[4],
+                                           const f32x4 (&dd)[4], int r0, int lgG, int my_key, int half,
+                                           float scale_log2, bf16x8 (&pb)[2], bf16x8 (&db)[2]) {
+  float p[16], ds[16];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int i = 4 * a + c;
-      float x = fmaf(s[i], scale_log2, -l2[c]);
-      if (MASK) x = my_key <= ((r0 + rr + c) >> lgG) ? x : -INFINITY;
+      float x = fmaf(s[i], scale_log2, -l2[a][c]);
+      if (MASK) x = my_key <= ((r0 + 32 * J + 8 * a + 4 * half + c) >> lgG) ? x : -INFINITY;
       p[i] = fast_exp2(x);
-      ds[i] = p[i] * (dp[i] - dd[c]);
+      ds[i] = p[i] * (dp[i] - dd[a][c]);
     }
-  }
-  bf16x8 pb[2], db[2];
   pack16(p, pb);
   pack16(ds, db);
-  lds_ready(tt);
+}
+
+template <int D>
+__device__ __forceinline__ void kv_accumulate(f32x16 (&dka)[D / 32], f32x16 (&dva)[D / 32],
+                                              const bf16x8 (&tt)[4 * (D / 32)], const bf16x8 (&pb)[2],
+                                              const bf16x8 (&db)[2]) {
+  constexpr int NT = D / 32;
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -688,16 +704,55 @@ __device__ __forceinline__ void kv_block(f32x16 (&dka)[D / 32], f32x16 (&dva)[D 
     }
 }
 
+// Ask the scheduler to alternate the region's N matrix products with its vector
+// instructions (one product, then up to K vector ops).
+template <int N, int K>
+__device__ __forceinline__ void interleave() {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, K, 0);
+  }
+}
+
+// One 64-row tile against the wave's 32 keys, as a two-block software pipeline:
+// the second block's score products are interleaved with the first block's
+// weights, and the first block's gradient products with the second block's
+// weights, so that the vector work runs while the matrix cores are busy.
 template <int D, bool MASK>
 __device__ __forceinline__ void kv_tile(f32x16 (&dka)[D / 32], f32x16 (&dva)[D / 32], const bf16x8 (&kf)[D / 16],
                                         const bf16x8 (&vf)[D / 16], const TileReads<D>& qa, uint32_t stat, int r0,
                                         int lgG, int my_key, int half, float scale_log2) {
   constexpr int DO = RowStage<D>::DO - RowStage<D>::Q;
+  constexpr int NT = D / 32;
   bf16x8 aq[D / 16], ao[D / 16];
+  f32x16 s0, dp0, s1, dp1;
+  f32x4 l2[4], dd[4];
+  bf16x8 tt[4 * NT];
+  bf16x8 pb0[2], db0[2], pb1[2], db1[2];
   load_rows<D>(aq, ao, qa, 0, DO);
+  kv_stats<D, 0>(stat, half, l2, dd);
   __builtin_amdgcn_sched_barrier(0);
-  kv_block<D, MASK, 0>(dka, dva, kf, vf, aq, ao, qa, stat, r0, lgG, my_key, half, scale_log2);
-  kv_block<D, MASK, 1>(dka, dva, kf, vf, aq, ao, qa, stat, r0, lgG, my_key, half, scale_log2);
+  kv_scores<D>(aq, ao, kf, vf, s0, dp0);
+  load_rows<D>(aq, ao, qa, 32 * Tile<D>::ROW_BYTES, DO);
+  kv_fetch_tr<D, 0>(tt, qa);
+  __builtin_amdgcn_sched_barrier(0);
+  // region A: block 1's scores beside block 0's weights
+  kv_scores<D>(aq, ao, kf, vf, s1, dp1);
+  kv_weights<0, MASK>(s0, dp0, l2, dd, r0, lgG, my_key, half, scale_log2, pb0, db0);
+  interleave<D / 8, 6>();
+  __builtin_amdgcn_sched_barrier(0);
+  kv_stats<D, 1>(stat, half, l2, dd);
+  lds_ready(tt);
+  __builtin_amdgcn_sched_barrier(0);
+  // region B: block 0's gradient products beside block 1's weights
+  kv_accumulate<D>(dka, dva, tt, pb0, db0);
+  kv_weights<1, MASK>(s1, dp1, l2, dd, r0, lgG, my_key, half, scale_log2, pb1, db1);
+  interleave<4 * NT, 6>();
+  __builtin_amdgcn_sched_barrier(0);
+  kv_fetch_tr<D, 1>(tt, qa);
+  lds_ready(tt);
+  kv_accumulate<D>(dka, dva, tt, pb1, db1);
 }
 
 template <int D, bool CAUSAL>
