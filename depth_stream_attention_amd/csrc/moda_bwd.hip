@@ -69,25 +69,6 @@ __device__ __forceinline__ s16x4 read_tr(uint32_t addr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_at<lds_s16x4_t>(addr));
 }
 
-// Transposed LDS reads issued as inline asm.  As a compiler builtin every such
-// read first waits for all outstanding direct-to-LDS loads (the compiler
-// cannot tell that those fill the other buffer), which exposes the next
-// tile's load latency in every tile.  The compiler does not track these
-// reads, so their consumers must follow lds_ready() on the same values.
-__device__ __forceinline__ s16x4 read_tr_async(uint32_t addr) {
-  s16x4 r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
-  return r;
-}
-// Wait until every LDS read of this wave has returned; afterwards the values
-// passed here may be used (each is re-defined after the wait).
-template <int N>
-__device__ __forceinline__ void lds_ready(bf16x8 (&x)[N]) {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(x[i]));
-}
-
 // ---- 64-row tiles read both row-wise and transposed -----------------------------
 //
 // Logical 16-byte chunk c of tile row r lives at physical chunk c ^ swz_u(r),

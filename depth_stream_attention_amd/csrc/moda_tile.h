@@ -179,6 +179,25 @@ __device__ __forceinline__ void pv_group(RowState<D>& st, const bf16x8& pb, cons
   }
 }
 
+// Transposed LDS reads issued as inline asm.  As a compiler builtin every such
+// read first waits for all outstanding direct-to-LDS loads (the compiler
+// cannot tell that those fill another buffer), which exposes the next tile's
+// load latency in every tile.  The compiler does not track these reads, so
+// their consumers must follow lds_ready() on the same values.
+__device__ __forceinline__ s16x4 read_tr_async(uint32_t addr) {
+  s16x4 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
+  return r;
+}
+// Wait until every LDS read of this wave has returned; afterwards the values
+// passed here may be used (each is re-defined after the wait).
+template <int N>
+__device__ __forceinline__ void lds_ready(bf16x8 (&x)[N]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(x[i]));
+}
+
 // Publish the tile this wave's DMA loads filled: wait for them, then barrier.
 __device__ __forceinline__ void publish_tile() {
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
