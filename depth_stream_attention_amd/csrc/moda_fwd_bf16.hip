@@ -176,9 +176,10 @@ __device__ __forceinline__ TileAddr<D> tile_addr(const lds_u8* buf, const LaneOf
   return a;
 }
 
-// One 64-key sequence tile: two 32-key blocks of S^T, each folded into the
-// state and multiplied into O^T.  MASK applies the causal / sequence-end mask
-// (branch-free selects); interior tiles take MASK = false.
+// One 64-key sequence tile: both 32-key blocks of S^T, then one online update
+// of the state for all 64 keys (one row max, one rescale test), then O^T +=
+// V^T P^T over the tile's four 16-key groups.  MASK applies the causal /
+// sequence-end mask (branch-free selects); interior tiles take MASK = false.
 template <int D, bool MASK, bool CAUSAL>
 __device__ __forceinline__ void seq_tile(RowState<D>& st, const bf16x8 (&qf)[D / 16], const TileAddr<D>& ta,
                                          int kt0, int T, int my_t, int half, float scale) {
@@ -186,24 +187,23 @@ __device__ __forceinline__ void seq_tile(RowState<D>& st, const bf16x8 (&qf)[D /
   f32x16 sq[2];
   sq[0] = qk_block<D>(qf, ta.k, 0);
   sq[1] = qk_block<D>(qf, ta.k, 32 * TL::ROW_BYTES);
+  // One online update for the whole 64-key tile: one row max, one rescale test.
+  float s[32];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const f32x16 sacc = sq[j];
-    float s[16];
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      s[i] = sacc[i];
+      s[16 * j + i] = sq[j][i];
       if (MASK) {
         const int key = kt0 + 32 * j + 8 * (i >> 2) + 4 * half + (i & 3);
         const bool vis = key < T && (!CAUSAL || key <= my_t);
-        s[i] = vis ? s[i] : -INFINITY;
+        s[16 * j + i] = vis ? s[16 * j + i] : -INFINITY;
       }
     }
-    bf16x8 pb[2];
-    online_update<D, 16>(st, s, pb, scale);
+  bf16x8 pb[4];
+  online_update<D, 32>(st, s, pb, scale);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) pv_group<D>(st, pb[h], ta.v, (32 * j + 16 * h) * TL::ROW_BYTES);
-  }
+  for (int g = 0; g < 4; ++g) pv_group<D>(st, pb[g], ta.v, 16 * g * TL::ROW_BYTES);
 }
 
 template <int D, bool DEPTH, bool CAUSAL>
