@@ -281,21 +281,35 @@ __global__ __launch_bounds__(kThreads) void moda_bwd_depth_kernel(
     for (int dc = 0; dc < DC; ++dc) dqa[dc] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     const int64_t slab = u * static_cast<int64_t>(L) * D;  // packed [B][T][Hk][L][d]: slab index = u
 
+    // Depth K/V rows of one 16-slot step (zero past slot L), the next step's
+    // loads issued before this step's products.
+    auto load_step = [&](int c0, bf16x8 (&kx)[KC], bf16x8 (&vx)[KC]) {
+      const int slot = c0 + r16;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
+        if (slot < L) {
+          a = *reinterpret_cast<const u32x4*>(kd + slab + static_cast<int64_t>(slot) * D + (4 * kc + grp) * 8);
+          c = *reinterpret_cast<const u32x4*>(vd + slab + static_cast<int64_t>(slot) * D + (4 * kc + grp) * 8);
+        }
+        kx[kc] = __builtin_bit_cast(bf16x8, a);
+        vx[kc] = __builtin_bit_cast(bf16x8, c);
+      }
+    };
+    bf16x8 kn[KC], vn[KC];
+    load_step(0, kn, vn);
     for (int c0 = 0; c0 < L; c0 += 16) {
       const int slot = c0 + r16;
       const bool valid = slot < L;
       bf16x8 kf[KC], vf[KC];
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
-        if (valid) {
-          a = *reinterpret_cast<const u32x4*>(kd + slab + static_cast<int64_t>(slot) * D + (4 * kc + grp) * 8);
-          c = *reinterpret_cast<const u32x4*>(vd + slab + static_cast<int64_t>(slot) * D + (4 * kc + grp) * 8);
-        }
-        kf[kc] = __builtin_bit_cast(bf16x8, a);
-        vf[kc] = __builtin_bit_cast(bf16x8, c);
-        *lds_at<lds_bf16x8_t>(ks + nrm[kc]) = kf[kc];
+        kf[kc] = kn[kc];
+        vf[kc] = vn[kc];
       }
+      if (c0 + 16 < L) load_step(c0 + 16, kn, vn);
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) *lds_at<lds_bf16x8_t>(ks + nrm[kc]) = kf[kc];
       f32x4 S = {}, dP = {}, ST = {}, dPT = {};
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
