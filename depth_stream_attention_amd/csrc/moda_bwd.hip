@@ -611,16 +611,7 @@ __device__ __forceinline__ void load_rows(bf16x8 (&aq)[D / 16], bf16x8 (&ao)[D /
   }
 }
 
-// A transposed A operand (two async reads) at a compile-time byte offset, which
-// goes into the instructions' offset field instead of costing an address add.
-template <int OFF>
-__device__ __forceinline__ s16x4 read_tr_async_at(uint32_t addr) {
-  static_assert(OFF >= 0 && OFF < 65536, "LDS instruction offset field");
-  s16x4 r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
-  return r;
-}
-
+// A transposed A operand (two async reads) at a compile-time byte offset.
 template <int D, int OFF>
 __device__ __forceinline__ bf16x8 read_tr8(const TileReads<D>& ta, int dt) {
   const s16x4 lo4 = read_tr_async_at<OFF>(ta.lo[dt]);
@@ -697,17 +688,6 @@ __device__ __forceinline__ void kv_accumulate(f32x16 (&dka)[D / 32], f32x16 (&dv
       dva[dt] = mfma32(tt[(2 * h) * NT + dt], pb[h], dva[dt]);
       dka[dt] = mfma32(tt[(2 * h + 1) * NT + dt], db[h], dka[dt]);
     }
-}
-
-// Ask the scheduler to alternate the region's N matrix products with its vector
-// instructions (one product, then up to K vector ops).
-template <int N, int K>
-__device__ __forceinline__ void interleave() {
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, K, 0);
-  }
 }
 
 // One 64-row tile against the wave's 32 keys, as a two-block software pipeline:

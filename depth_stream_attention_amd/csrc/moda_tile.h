@@ -189,13 +189,40 @@ __device__ __forceinline__ s16x4 read_tr_async(uint32_t addr) {
   asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
   return r;
 }
+// The same at a compile-time byte offset, which goes into the instruction's
+// offset field instead of costing an address add.
+template <int OFF>
+__device__ __forceinline__ s16x4 read_tr_async_at(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "LDS instruction offset field");
+  s16x4 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
 // Wait until every LDS read of this wave has returned; afterwards the values
 // passed here may be used (each is re-defined after the wait).
+__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// Re-define values after lds_wait(), so that their consumers cannot be placed
+// before it.
 template <int N>
-__device__ __forceinline__ void lds_ready(bf16x8 (&x)[N]) {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+__device__ __forceinline__ void lds_tie(bf16x8 (&x)[N]) {
 #pragma unroll
   for (int i = 0; i < N; ++i) asm volatile("" : "+v"(x[i]));
+}
+template <int N>
+__device__ __forceinline__ void lds_ready(bf16x8 (&x)[N]) {
+  lds_wait();
+  lds_tie(x);
+}
+
+// Ask the scheduler to alternate the region's N matrix products with its vector
+// instructions (one product, then up to K vector ops).
+template <int N, int K>
+__device__ __forceinline__ void interleave() {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, K, 0);
+  }
 }
 
 // Publish the tile this wave's DMA loads filled: wait for them, then barrier.
