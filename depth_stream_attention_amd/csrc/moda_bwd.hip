@@ -31,6 +31,8 @@
 // patterns free of bank conflicts.
 #include <algorithm>
 
+#include <type_traits>
+
 #include "moda_launch.h"
 #include "moda_tile.h"
 
@@ -619,17 +621,17 @@ __device__ __forceinline__ bf16x8 read_tr8(const TileReads<D>& ta, int dt) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-template <int D, int J>
+template <int D, int J, int B>
 __device__ __forceinline__ void kv_fetch_tr(bf16x8 (&tt)[4 * (D / 32)], const TileReads<D>& qa) {
   using TL = Tile<D>;
   constexpr int DO = RowStage<D>::DO - RowStage<D>::Q;
   constexpr int NT = D / 32;
 #pragma unroll
   for (int dt = 0; dt < NT; ++dt) {
-    tt[0 * NT + dt] = read_tr8<D, (32 * J) * TL::ROW_BYTES + DO>(qa, dt);
-    tt[1 * NT + dt] = read_tr8<D, (32 * J) * TL::ROW_BYTES>(qa, dt);
-    tt[2 * NT + dt] = read_tr8<D, (32 * J + 16) * TL::ROW_BYTES + DO>(qa, dt);
-    tt[3 * NT + dt] = read_tr8<D, (32 * J + 16) * TL::ROW_BYTES>(qa, dt);
+    tt[0 * NT + dt] = read_tr8<D, B + (32 * J) * TL::ROW_BYTES + DO>(qa, dt);
+    tt[1 * NT + dt] = read_tr8<D, B + (32 * J) * TL::ROW_BYTES>(qa, dt);
+    tt[2 * NT + dt] = read_tr8<D, B + (32 * J + 16) * TL::ROW_BYTES + DO>(qa, dt);
+    tt[3 * NT + dt] = read_tr8<D, B + (32 * J + 16) * TL::ROW_BYTES>(qa, dt);
   }
 }
 
@@ -694,10 +696,13 @@ __device__ __forceinline__ void kv_accumulate(f32x16 (&dka)[D / 32], f32x16 (&dv
 // the second block's score products are interleaved with the first block's
 // weights, and the first block's gradient products with the second block's
 // weights, so that the vector work runs while the matrix cores are busy.
-template <int D, bool MASK>
+// qa holds the read addresses of stage buffer 0 and stat its base; the tile
+// sits B bytes further (a constant, carried in the instructions' offsets).
+template <int D, bool MASK, int B>
 __device__ __forceinline__ void kv_tile(f32x16 (&dka)[D / 32], f32x16 (&dva)[D / 32], const bf16x8 (&kf)[D / 16],
-                                        const bf16x8 (&vf)[D / 16], const TileReads<D>& qa, uint32_t stat, int r0,
+                                        const bf16x8 (&vf)[D / 16], const TileReads<D>& qa, uint32_t stat0, int r0,
                                         int lgG, int my_key, int half, float scale_log2) {
+  const uint32_t stat = stat0 + B;
   constexpr int DO = RowStage<D>::DO - RowStage<D>::Q;
   constexpr int NT = D / 32;
   bf16x8 aq[D / 16], ao[D / 16];
@@ -705,12 +710,12 @@ __device__ __forceinline__ void kv_tile(f32x16 (&dka)[D / 32], f32x16 (&dva)[D /
   f32x4 l2[4], dd[4];
   bf16x8 tt[4 * NT];
   bf16x8 pb0[2], db0[2], pb1[2], db1[2];
-  load_rows<D>(aq, ao, qa, 0, DO);
+  load_rows<D>(aq, ao, qa, B, DO);
   kv_stats<D, 0>(stat, half, l2, dd);
   __builtin_amdgcn_sched_barrier(0);
   kv_scores<D>(aq, ao, kf, vf, s0, dp0);
-  load_rows<D>(aq, ao, qa, 32 * Tile<D>::ROW_BYTES, DO);
-  kv_fetch_tr<D, 0>(tt, qa);
+  load_rows<D>(aq, ao, qa, B + 32 * Tile<D>::ROW_BYTES, DO);
+  kv_fetch_tr<D, 0, B>(tt, qa);
   __builtin_amdgcn_sched_barrier(0);
   // region A: block 1's scores beside block 0's weights
   kv_scores<D>(aq, ao, kf, vf, s1, dp1);
@@ -725,7 +730,7 @@ __device__ __forceinline__ void kv_tile(f32x16 (&dka)[D / 32], f32x16 (&dva)[D /
   kv_weights<1, MASK>(s1, dp1, l2, dd, r0, lgG, my_key, half, scale_log2, pb1, db1);
   interleave<4 * NT, 6>();
   __builtin_amdgcn_sched_barrier(0);
-  kv_fetch_tr<D, 1>(tt, qa);
+  kv_fetch_tr<D, 1, B>(tt, qa);
   lds_ready(tt);
   kv_accumulate<D>(dka, dva, tt, pb1, db1);
 }
@@ -784,30 +789,45 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
   }
 
   // Row tiles: causal rows see key j from token j on, so tiles start at the
-  // block's first key; those before token k0 + kKB - 1 need the mask.
+  // block's first key; those before token k0 + kKB - 1 need the mask.  The
+  // masked run is extended to an even length (the mask keeps every pair of an
+  // unmasked tile) so that both loops take tiles in pairs, the first of each
+  // pair in stage buffer 0: every LDS address is then a per-lane offset plus
+  // an instruction immediate.
   const int nt = (TG + kBN - 1) / kBN;
   const int i0 = CAUSAL ? (k0 << lgG) / kBN : 0;
-  const int i_m = CAUSAL ? min(nt, (((k0 + kKB - 1) << lgG) + kBN - 1) / kBN) : i0;
-  auto buf_of = [&](int pos) -> lds_u8* { return smem + opaque_s((pos & 1) * RS::BYTES); };
+  const int i_m0 = CAUSAL ? min(nt, (((k0 + kKB - 1) << lgG) + kBN - 1) / kBN) : i0;
+  const int i_m = min(nt, i0 + ((i_m0 - i0 + 1) & ~1));
+  const uint32_t lds0 = lds_addr(smem);
+  const TileReads<D> ra = at<D>(ro, lds0 + RS::Q);  // stage buffer 0
 
-  int pos = 0, it = i0;
-  if (i0 < nt) dma_rows<D>(qb, ob, l2b, ddb, T, Hq, lgG, TG, i0, smem, wave, lane, dm);
-  for (; it < i_m; ++it, ++pos) {  // masked tiles
-    lds_u8* cur = buf_of(pos);
+  // One tile in stage buffer P (the next one is loaded into buffer 1 - P).
+  auto tile = [&](auto parity, auto maskc, int it) __attribute__((always_inline)) {
+    constexpr int P = decltype(parity)::value;
+    constexpr bool MASK = decltype(maskc)::value != 0;
     publish_tile();
-    if (it + 1 < nt) dma_rows<D>(qb, ob, l2b, ddb, T, Hq, lgG, TG, it + 1, buf_of(pos + 1), wave, lane, dm);
+    if (it + 1 < nt)
+      dma_rows<D>(qb, ob, l2b, ddb, T, Hq, lgG, TG, it + 1, smem + opaque_s((1 - P) * RS::BYTES), wave, lane, dm);
     const int r0 = it * kBN;
-    if (((r0 + kBN - 1) >> lgG) < kw0) continue;  // no row of this tile sees the wave's keys
-    const uint32_t base = lds_addr(cur);
-    kv_tile<D, true>(dka, dva, kf, vf, at<D>(ro, base + RS::Q), base, r0, lgG, my_key, half, scale_log2);
+    if (MASK && ((r0 + kBN - 1) >> lgG) < kw0) return;  // no row of this tile sees the wave's keys
+    kv_tile<D, MASK, P * RS::BYTES>(dka, dva, kf, vf, ra, lds0, r0, lgG, my_key, half, scale_log2);
+  };
+
+  int it = i0;
+  if (i0 < nt) dma_rows<D>(qb, ob, l2b, ddb, T, Hq, lgG, TG, i0, smem, wave, lane, dm);
+  for (; it + 1 < i_m; it += 2) {  // masked tiles (an even number of them, unless the rows run out)
+    tile(std::integral_constant<int, 0>(), std::integral_constant<int, 1>(), it);
+    tile(std::integral_constant<int, 1>(), std::integral_constant<int, 1>(), it + 1);
   }
-  for (; it < nt; ++it, ++pos) {  // unmasked tiles
-    lds_u8* cur = buf_of(pos);
-    publish_tile();
-    if (it + 1 < nt) dma_rows<D>(qb, ob, l2b, ddb, T, Hq, lgG, TG, it + 1, buf_of(pos + 1), wave, lane, dm);
-    const uint32_t base = lds_addr(cur);
-    kv_tile<D, false>(dka, dva, kf, vf, at<D>(ro, base + RS::Q), base, it * kBN, lgG, my_key, half, scale_log2);
+  if (it < i_m) {  // only when i_m == nt
+    tile(std::integral_constant<int, 0>(), std::integral_constant<int, 1>(), it);
+    ++it;
   }
+  for (; it + 1 < nt; it += 2) {  // unmasked tiles
+    tile(std::integral_constant<int, 0>(), std::integral_constant<int, 0>(), it);
+    tile(std::integral_constant<int, 1>(), std::integral_constant<int, 0>(), it + 1);
+  }
+  if (it < nt) tile(std::integral_constant<int, 0>(), std::integral_constant<int, 0>(), it);
 
   if (my_key < T) {
     uint16_t* krow = dk + koff;
