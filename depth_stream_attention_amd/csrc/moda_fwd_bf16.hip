@@ -40,6 +40,8 @@
 //     FMA; the output rescale is skipped unless a row max grows by more than
 //     2^8.  lse is converted back to the natural log at the end.
 //   * Causal workgroups are issued heaviest first (last row block first).
+#include <type_traits>
+
 #include "moda_launch.h"
 #include "moda_tile.h"
 
@@ -282,9 +284,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // wave/2, score registers [8*(wave%2), 8*(wave%2) + 8).
   const int dj = wave >> 1, dh = wave & 1;
 
-  // The LDS buffer of pipeline position pos is smem + (pos & 1) * 2 * BYTES.  Its
-  // base is hidden from the optimiser so that the per-tile address adds stay
-  // in the loop instead of becoming two hoisted copies of every offset.
+  // The LDS buffer of pipeline position pos is smem + (pos & 1) * 2 * BYTES.
+  // Sequence tiles run in pairs with a constant buffer each (seq_run); the
+  // depth tiles, one per run, take the buffer at run time, with its base
+  // hidden from the optimiser so that their address adds stay in place
+  // instead of becoming hoisted copies of every offset.
   auto buf_of = [&](int pos) -> lds_u8* {
     return smem + opaque_s((pos & 1) * (2 * TL::BYTES));
   };
@@ -300,6 +304,38 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int n_int = CAUSAL ? min(ns, (tb + 1) / kBN) : T / kBN;
   int pos = 0;  // pipeline position: selects the LDS buffer
   int sq = 0;   // next sequence tile
+  // One sequence tile in LDS buffer P (= pos % 2, a constant here, so the
+  // tile's read addresses are the per-lane offsets plus instruction
+  // immediates); the next tile -- sequence tile sq + 1 of the run ending at
+  // s_end, else depth tile d if d < nd -- is loaded into buffer 1 - P.
+  auto seq_step = [&](auto parity, auto maskc, int s_end, int d) __attribute__((always_inline)) {
+    constexpr int P = decltype(parity)::value;
+    constexpr bool MASK = decltype(maskc)::value != 0;
+    lds_u8* const nxt = smem + opaque_s((1 - P) * (2 * TL::BYTES));
+    publish_tile();
+    if (sq + 1 < s_end || (d >= nd && sq + 1 < ns))
+      dma_seq<D>(kb, vb, seq_range, g.key_bytes, Hk, sq + 1, nxt, wave, lo);
+    else if (DEPTH && d < nd)
+      dma_depth<D>(g, d, nchunk, nxt, wave, lane);
+    const int kt0 = sq * kBN;
+    ++sq;
+    ++pos;
+    if (MASK && CAUSAL && kt0 > wt1) return;  // nothing visible to this wave
+    seq_tile<D, MASK, CAUSAL>(st, qf, tile_addr<D>(smem + P * (2 * TL::BYTES), lo), kt0, T, my_t, half,
+                              scale_log2);
+  };
+  // Sequence tiles sq .. s_end - 1 in pairs (buffer 0, then buffer 1), after
+  // at most one tile that brings pos to an even value.
+  auto seq_run = [&](auto maskc, int s_end, int d) __attribute__((always_inline)) {
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    if (sq < s_end && (pos & 1)) seq_step(P1(), maskc, s_end, d);
+    while (sq + 1 < s_end) {
+      seq_step(P0(), maskc, s_end, d);
+      seq_step(P1(), maskc, s_end, d);
+    }
+    if (sq < s_end) seq_step(P0(), maskc, s_end, d);
+  };
   if (DEPTH && nd > 0 && n_int / max(nd, 1) == 0)
     dma_depth<D>(g, 0, nchunk, smem, wave, lane);
   else
@@ -308,16 +344,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   if constexpr (DEPTH) {
     for (int d = 0; d < nd; ++d) {
       const int s_end = ((d + 1) * n_int) / nd;
-      for (; sq < s_end; ++sq, ++pos) {
-        lds_u8* cur = buf_of(pos);
-        lds_u8* nxt = buf_of(pos + 1);
-        publish_tile();
-        if (sq + 1 < s_end)
-          dma_seq<D>(kb, vb, seq_range, g.key_bytes, Hk, sq + 1, nxt, wave, lo);
-        else
-          dma_depth<D>(g, d, nchunk, nxt, wave, lane);
-        seq_tile<D, false, CAUSAL>(st, qf, tile_addr<D>(cur, lo), sq * kBN, T, my_t, half, scale_log2);
-      }
+      seq_run(std::integral_constant<int, 0>(), s_end, d);
       // depth tile d: each wave sees only its own token's slots
       lds_u8* cur = buf_of(pos);
       lds_u8* nxt = buf_of(pos + 1);
@@ -348,22 +375,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       pv_group<D>(st, pb[0], ta.v, (32 * dj + 16 * dh) * TL::ROW_BYTES);
     }
   }
-  for (; sq < n_int; ++sq, ++pos) {  // unmasked sequence tiles (all of them when there is no depth)
-    lds_u8* cur = buf_of(pos);
-    lds_u8* nxt = buf_of(pos + 1);
-    publish_tile();
-    if (sq + 1 < ns) dma_seq<D>(kb, vb, seq_range, g.key_bytes, Hk, sq + 1, nxt, wave, lo);
-    seq_tile<D, false, CAUSAL>(st, qf, tile_addr<D>(cur, lo), sq * kBN, T, my_t, half, scale_log2);
-  }
-  for (; sq < ns; ++sq, ++pos) {  // masked sequence tiles
-    lds_u8* cur = buf_of(pos);
-    lds_u8* nxt = buf_of(pos + 1);
-    publish_tile();
-    if (sq + 1 < ns) dma_seq<D>(kb, vb, seq_range, g.key_bytes, Hk, sq + 1, nxt, wave, lo);
-    const int kt0 = sq * kBN;
-    if (CAUSAL && kt0 > wt1) continue;  // nothing visible to this wave
-    seq_tile<D, true, CAUSAL>(st, qf, tile_addr<D>(cur, lo), kt0, T, my_t, half, scale_log2);
-  }
+  seq_run(std::integral_constant<int, 0>(), n_int, nd);  // unmasked sequence tiles (all of them without depth)
+  seq_run(std::integral_constant<int, 1>(), ns, nd);     // masked sequence tiles
 
   // ---- epilogue --------------------------------------------------------------
   const float l_tot = pair_sum(st.l);
