@@ -397,16 +397,17 @@ __device__ __forceinline__ void dma_kv(const uint16_t* kb, const uint16_t* vb, u
 }
 
 // One 64-key tile: for both 32-key blocks S^T, dP^T, dS^T, then dQ^T += K^T dS^T.
-template <int D, bool MASK, bool CAUSAL>
+// ka, va address buffer 0's K and V; the tile sits B bytes further.
+template <int D, bool MASK, bool CAUSAL, int B>
 __device__ __forceinline__ void dq_tile(f32x16 (&dqa)[D / 32], const bf16x8 (&qf)[D / 16], const bf16x8 (&df)[D / 16],
                                         const TileReads<D>& ka, const TileReads<D>& va, int kt0, int T, int my_t,
                                         int half, float scale_log2, float l2, float dd) {
   using TL = Tile<D>;
   f32x16 sq[2], dp[2];
-  sq[0] = qk_block<D>(qf, ka.nr, 0);
-  sq[1] = qk_block<D>(qf, ka.nr, 32 * TL::ROW_BYTES);
-  dp[0] = qk_block<D>(df, va.nr, 0);
-  dp[1] = qk_block<D>(df, va.nr, 32 * TL::ROW_BYTES);
+  sq[0] = qk_block<D>(qf, ka.nr, B);
+  sq[1] = qk_block<D>(qf, ka.nr, B + 32 * TL::ROW_BYTES);
+  dp[0] = qk_block<D>(df, va.nr, B);
+  dp[1] = qk_block<D>(df, va.nr, B + 32 * TL::ROW_BYTES);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     float ds[16];
@@ -423,7 +424,7 @@ __device__ __forceinline__ void dq_tile(f32x16 (&dqa)[D / 32], const bf16x8 (&qf
     bf16x8 pb[2];
     pack16(ds, pb);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) acc_group<D>(dqa, pb[h], ka, (32 * j + 16 * h) * TL::ROW_BYTES);
+    for (int h = 0; h < 2; ++h) acc_group<D>(dqa, pb[h], ka, B + (32 * j + 16 * h) * TL::ROW_BYTES);
   }
 }
 
@@ -490,33 +491,41 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) dqa[dt] = f32x16{};
 
-  auto buf_of = [&](int pos) -> lds_u8* { return smem + opaque_s((pos & 1) * (2 * TL::BYTES)); };
-  auto reads_of = [&](lds_u8* buf, TileReads<D>& ka, TileReads<D>& va) {
-    ka = at<D>(ro, lds_addr(buf));
-    va = at<D>(ro, lds_addr(buf) + TL::BYTES);
-  };
-
-  const int n_int = CAUSAL ? min(ns, (tb + 1) / kBN) : T / kBN;
-  int pos = 0, sq = 0;
-  dma_kv<D>(kb, vb, seq_range, key_bytes, Hk, 0, smem, wave, dm);
-  for (; sq < n_int; ++sq, ++pos) {
-    lds_u8* cur = buf_of(pos);
+  // Tiles run in pairs (LDS buffer 0, then buffer 1, after at most one tile
+  // that evens the position), so every read address is a per-lane offset of
+  // buffer 0 plus an instruction immediate.  The last unmasked tile of an odd
+  // run is taken as masked (the mask keeps all of it), so that both runs
+  // start at an even position.
+  const uint32_t lds0 = lds_addr(smem);
+  const TileReads<D> ka0 = at<D>(ro, lds0), va0 = at<D>(ro, lds0 + TL::BYTES);
+  const int n_int0 = CAUSAL ? min(ns, (tb + 1) / kBN) : T / kBN;
+  const int n_int = n_int0 & ~1;
+  int sq = 0;
+  auto tile = [&](auto parity, auto maskc) __attribute__((always_inline)) {
+    constexpr int P = decltype(parity)::value;
+    constexpr bool MASK = decltype(maskc)::value != 0;
     publish_tile();
-    if (sq + 1 < ns) dma_kv<D>(kb, vb, seq_range, key_bytes, Hk, sq + 1, buf_of(pos + 1), wave, dm);
-    TileReads<D> ka, va;
-    reads_of(cur, ka, va);
-    dq_tile<D, false, CAUSAL>(dqa, qf, df, ka, va, sq * kBN, T, my_t, half, scale_log2, l2, dd);
-  }
-  for (; sq < ns; ++sq, ++pos) {
-    lds_u8* cur = buf_of(pos);
-    publish_tile();
-    if (sq + 1 < ns) dma_kv<D>(kb, vb, seq_range, key_bytes, Hk, sq + 1, buf_of(pos + 1), wave, dm);
+    if (sq + 1 < ns)
+      dma_kv<D>(kb, vb, seq_range, key_bytes, Hk, sq + 1, smem + opaque_s((1 - P) * (2 * TL::BYTES)), wave, dm);
     const int kt0 = sq * kBN;
-    if (CAUSAL && kt0 > wt1) continue;
-    TileReads<D> ka, va;
-    reads_of(cur, ka, va);
-    dq_tile<D, true, CAUSAL>(dqa, qf, df, ka, va, kt0, T, my_t, half, scale_log2, l2, dd);
+    ++sq;
+    if (MASK && CAUSAL && kt0 > wt1) return;
+    dq_tile<D, MASK, CAUSAL, P * 2 * TL::BYTES>(dqa, qf, df, ka0, va0, kt0, T, my_t, half, scale_log2, l2, dd);
+  };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  using U = std::integral_constant<int, 0>;
+  using M = std::integral_constant<int, 1>;
+  dma_kv<D>(kb, vb, seq_range, key_bytes, Hk, 0, smem, wave, dm);
+  while (sq + 1 < n_int) {  // unmasked tiles
+    tile(P0(), U());
+    tile(P1(), U());
   }
+  while (sq + 1 < ns) {  // masked tiles
+    tile(P0(), M());
+    tile(P1(), M());
+  }
+  if (sq < ns) tile(P0(), M());
 
   if (row_ok) {
     uint16_t* orow = dq + qoff;
@@ -571,7 +580,6 @@ template <int D>
 __device__ __forceinline__ void dma_rows(const uint16_t* qb, const uint16_t* ob, const float* l2b, const float* ddb,
                                          int T, int Hq, int lgG, int TG, int idx, lds_u8* buf, int wave, int lane,
                                          const RowDma<D>& o) {
-  using TL = Tile<D>;
   using RS = RowStage<D>;
   constexpr int NX = kNX<D>;
   const int r0 = idx * kBN;
@@ -740,7 +748,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ ws_l2, const float* __restrict__ ws_dd, int B, int T,
     int Hq, int Hk, int lgG, float scale, float scale_log2, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
-  using TL = Tile<D>;
   using RS = RowStage<D>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[2 * RS::BYTES];
   lds_u8* const smem = (lds_u8*)smem_raw;
