@@ -22,15 +22,15 @@
 //             per wave, lane = query row) over 64-key sequence tiles:
 //             S^T = K Q^T, dP^T = V dO^T, dS^T, then dQ^T += K^T dS^T.  Adds the
 //             depth share and writes dq.
-//   4. dkv:   128 sequence keys per workgroup, 32 per wave (lane = key) over
-//             64-row tiles of Q, dO, lse and Dsum: S = Q K^T, dP = dO V^T, then
-//             dV^T += dO^T P and dK^T += Q^T dS.
+//   4. dkv:   128 sequence keys per workgroup over 64-row tiles of Q, dO, lse
+//             and Dsum; each 32 keys (lane = key) are shared by two waves, one
+//             forming S = Q K^T, P and dV^T += dO^T P, the other, a tile later,
+//             dP = dO V^T, dS from the P passed through LDS, and dK^T += Q^T dS.
 // Tiles are staged by direct-to-LDS buffer loads into a double-buffered
-// pipeline.  Every tile that is read both row-wise (as an MFMA operand) and
+// (dkv: triple-buffered) pipeline.  Every tile that is read both row-wise (as an MFMA operand) and
 // transposed (ds_read_b64_tr_b16) uses one XOR swizzle that keeps both read
 // patterns free of bank conflicts.
 #include <algorithm>
-
 #include <type_traits>
 
 #include "moda_launch.h"
@@ -40,6 +40,7 @@ namespace moda {
 namespace {
 
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4_t;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4_t;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
@@ -546,6 +547,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
 // ---- 4. dk, dv over the sequence keys --------------------------------------------------
 
+// Eight waves; waves w and w + 4 own the same 32 keys.  The P wave holds K^T
+// of its keys and the dV^T accumulator: per 64-row tile it forms S = Q K^T,
+// P = exp2(S*scale*log2e - lse2) (masked), writes P (bf16, in the register
+// layout of its accumulators) to LDS, and adds dO^T P into dV^T.  The dS wave
+// holds V^T and the dK^T accumulator: one tile later it forms dP = dO V^T,
+// reads P back (the same lane's layout), forms dS = P (dP - Dsum) from that
+// bf16 P (dS is rounded to bf16 for its product anyway), and adds Q^T dS
+// into dK^T.  Each wave holds one key operand and one accumulator (96
+// registers), so two waves share a SIMD; one barrier per tile publishes the
+// next row tile and the P of the previous one.  Row tiles rotate through three
+// stage buffers (tile i for the P waves, tile i-1 for the dS waves, tile i+1
+// loading), P through three transfer slots.
+
 // Direct-to-LDS staging of a 64-row tile of Q and dO (expanded rows: row
 // t*G + g at token offset t, head g) plus the tile's 64 lse2 and Dsum values.
 template <int D>
@@ -566,61 +580,6 @@ __device__ __forceinline__ void init_row_dma(RowDma<D>& o, int lane, int wave, i
   }
 }
 
-// LDS buffer layout of one stage: Q tile, dO tile, lse2[64], Dsum[64].
-template <int D>
-struct RowStage {
-  static constexpr int Q = 0;
-  static constexpr int DO = Tile<D>::BYTES;
-  static constexpr int L2 = 2 * Tile<D>::BYTES;
-  static constexpr int DD = L2 + kBN * 4;
-  static constexpr int BYTES = DD + kBN * 4;
-};
-
-template <int D>
-__device__ __forceinline__ void dma_rows(const uint16_t* qb, const uint16_t* ob, const float* l2b, const float* ddb,
-                                         int T, int Hq, int lgG, int TG, int idx, lds_u8* buf, int wave, int lane,
-                                         const RowDma<D>& o) {
-  using RS = RowStage<D>;
-  constexpr int NX = kNX<D>;
-  const int r0 = idx * kBN;
-  const int t0 = r0 >> lgG;
-  const int64_t first = static_cast<int64_t>(t0) * Hq * D;
-  const uint32_t range = static_cast<uint32_t>((static_cast<int64_t>(T - 1 - t0) * Hq + (1 << lgG)) * D * 2);
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qb + first, range);
-  const __amdgpu_buffer_rsrc_t ro = make_rsrc(ob + first, range);
-#pragma unroll
-  for (int x = 0; x < NX; ++x) {
-    lds_u8* dst = buf + (wave * NX + x) * 1024;
-    const uint32_t off = o.o[x];
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void_t*)(dst + RS::Q), 16, off, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ro, (lds_void_t*)(dst + RS::DO), 16, off, 0, 0, 0);
-  }
-  if (wave < 2) {
-    const float* src = (wave == 0 ? l2b : ddb) + r0;
-    const uint32_t frange = static_cast<uint32_t>(TG - r0) * 4;
-    const __amdgpu_buffer_rsrc_t rf =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(src), static_cast<short>(0), static_cast<int>(frange),
-                                          kBufFlags);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rf, (lds_void_t*)(buf + (wave == 0 ? RS::L2 : RS::DD)), 4,
-                                             static_cast<uint32_t>(lane) * 4, 0, 0, 0);
-  }
-}
-
-// One 64-row tile against the wave's 32 keys: for both 32-row blocks S = Q K^T,
-// dP = dO V^T, P and dS, then dV^T += dO^T P and dK^T += Q^T dS.  LDS operands
-// are fetched in groups ahead of the products that use them (the next block's
-// row operands while this block's weights are formed), so each product waits
-// on one group's latency, not on one read's per MFMA.
-template <int D>
-__device__ __forceinline__ void load_rows(bf16x8 (&aq)[D / 16], bf16x8 (&ao)[D / 16], const TileReads<D>& qa,
-                                          int off, int do_off) {
-#pragma unroll
-  for (int sl = 0; sl < D / 16; ++sl) {
-    aq[sl] = *lds_at<lds_bf16x8_t>(qa.nr[sl] + off);
-    ao[sl] = *lds_at<lds_bf16x8_t>(qa.nr[sl] + off + do_off);
-  }
-}
-
 // A transposed A operand (two async reads) at a compile-time byte offset.
 template <int D, int OFF>
 __device__ __forceinline__ bf16x8 read_tr8(const TileReads<D>& ta, int dt) {
@@ -629,154 +588,204 @@ __device__ __forceinline__ bf16x8 read_tr8(const TileReads<D>& ta, int dt) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-template <int D, int J, int B>
-__device__ __forceinline__ void kv_fetch_tr(bf16x8 (&tt)[4 * (D / 32)], const TileReads<D>& qa) {
+template <int D>
+struct XferSlot {
+  static constexpr int PAIR = 4 * 1024;  // 16 dwords per lane: 4 chunks of 64 lanes x 16 bytes
+  static constexpr int BYTES = 4 * PAIR;
+};
+
+// dO^T (P wave) or Q^T (dS wave) operands of one 32-row block, half h and d
+// tile dt at tt[h * NT + dt], from the stage at `stage` + SRC (async reads).
+template <int D, int J, int SRC>
+__device__ __forceinline__ void fetch_tr_block(bf16x8 (&tt)[2 * (D / 32)], const TileReads<D>& ta) {
   using TL = Tile<D>;
-  constexpr int DO = RowStage<D>::DO - RowStage<D>::Q;
   constexpr int NT = D / 32;
 #pragma unroll
   for (int dt = 0; dt < NT; ++dt) {
-    tt[0 * NT + dt] = read_tr8<D, B + (32 * J) * TL::ROW_BYTES + DO>(qa, dt);
-    tt[1 * NT + dt] = read_tr8<D, B + (32 * J) * TL::ROW_BYTES>(qa, dt);
-    tt[2 * NT + dt] = read_tr8<D, B + (32 * J + 16) * TL::ROW_BYTES + DO>(qa, dt);
-    tt[3 * NT + dt] = read_tr8<D, B + (32 * J + 16) * TL::ROW_BYTES>(qa, dt);
+    tt[dt] = read_tr8<D, SRC + (32 * J) * TL::ROW_BYTES>(ta, dt);
+    tt[NT + dt] = read_tr8<D, SRC + (32 * J + 16) * TL::ROW_BYTES>(ta, dt);
   }
 }
 
+// LDS layout: the three stages' Q tiles, then their dO
+// tiles, then their lse2 and Dsum rows, then the three transfer slots.  From a
+// role's base every tile it reads (row-wise or transposed) lies within the
+// 64 KiB reach of an instruction's immediate offset.
 template <int D>
-__device__ __forceinline__ void kv_scores(const bf16x8 (&aq)[D / 16], const bf16x8 (&ao)[D / 16],
-                                          const bf16x8 (&kf)[D / 16], const bf16x8 (&vf)[D / 16], f32x16& s,
-                                          f32x16& dp) {
-  s = f32x16{};
-  dp = f32x16{};
-#pragma unroll
-  for (int sl = 0; sl < D / 16; ++sl) {
-    s = mfma32(aq[sl], kf[sl], s);  // [row][key]
-    dp = mfma32(ao[sl], vf[sl], dp);
-  }
-}
+struct RowStages {
+  static constexpr int TB = Tile<D>::BYTES;
+  static constexpr int Q = 0;                      // + stage * TB
+  static constexpr int DO = 3 * TB;                // + stage * TB
+  static constexpr int ST = 6 * TB;                // + stage * SB: lse2[64], then Dsum[64]
+  static constexpr int SB = 2 * kBN * 4;
+  static constexpr int XF = ST + 3 * SB;           // + slot * XferSlot::BYTES
+  static constexpr int BYTES = XF + 3 * XferSlot<D>::BYTES;
+};
 
-// lse2 and Dsum of the 16 rows of block J this lane's score registers cover.
-template <int D, int J>
-__device__ __forceinline__ void kv_stats(uint32_t stat, int half, f32x4 (&l2)[4], f32x4 (&dd)[4]) {
-#pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int rr = 32 * J + 8 * a + 4 * half;  // tile rows rr .. rr+3 in registers 4a .. 4a+3
-    l2[a] = *lds_at<lds_f32x4_t>(stat + RowStage<D>::L2 + rr * 4);
-    dd[a] = *lds_at<lds_f32x4_t>(stat + RowStage<D>::DD + rr * 4);
-  }
-}
-
-template <int J, bool MASK>
-__device__ __forceinline__ void kv_weights(const f32x16& s, const f32x16& dp, const f32x4 (&l2)[4],
-                                           const f32x4 (&dd)[4], int r0, int lgG, int my_key, int half,
-                                           float scale_log2, bf16x8 (&pb)[2], bf16x8 (&db)[2]) {
-  float p[16], ds[16];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int i = 4 * a + c;
-      float x = fmaf(s[i], scale_log2, -l2[a][c]);
-      if (MASK) x = my_key <= ((r0 + 32 * J + 8 * a + 4 * half + c) >> lgG) ? x : -INFINITY;
-      p[i] = fast_exp2(x);
-      ds[i] = p[i] * (dp[i] - dd[a][c]);
-    }
-  pack16(p, pb);
-  pack16(ds, db);
-}
-
+// Direct-to-LDS loads of row tile idx into stage r.
 template <int D>
-__device__ __forceinline__ void kv_accumulate(f32x16 (&dka)[D / 32], f32x16 (&dva)[D / 32],
-                                              const bf16x8 (&tt)[4 * (D / 32)], const bf16x8 (&pb)[2],
-                                              const bf16x8 (&db)[2]) {
-  constexpr int NT = D / 32;
+__device__ __forceinline__ void dma_rows(const uint16_t* qb, const uint16_t* ob, const float* l2b, const float* ddb,
+                                          int T, int Hq, int lgG, int TG, int idx, lds_u8* smem, int r, int wave,
+                                          int lane, const RowDma<D>& o) {
+  using LY = RowStages<D>;
+  constexpr int NX = kNX<D>;
+  const int r0 = idx * kBN;
+  const int t0 = r0 >> lgG;
+  const int64_t first = static_cast<int64_t>(t0) * Hq * D;
+  const uint32_t range = static_cast<uint32_t>((static_cast<int64_t>(T - 1 - t0) * Hq + (1 << lgG)) * D * 2);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qb + first, range);
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(ob + first, range);
+  lds_u8* const qdst = smem + opaque_s(LY::Q + r * LY::TB + wave * NX * 1024);
+  lds_u8* const odst = smem + opaque_s(LY::DO + r * LY::TB + wave * NX * 1024);
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int dt = 0; dt < NT; ++dt) {
-      dva[dt] = mfma32(tt[(2 * h) * NT + dt], pb[h], dva[dt]);
-      dka[dt] = mfma32(tt[(2 * h + 1) * NT + dt], db[h], dka[dt]);
-    }
+  for (int x = 0; x < NX; ++x) {
+    const uint32_t off = o.o[x];
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void_t*)(qdst + x * 1024), 16, off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ro, (lds_void_t*)(odst + x * 1024), 16, off, 0, 0, 0);
+  }
+  if (wave < 2) {
+    const float* src = (wave == 0 ? l2b : ddb) + r0;
+    const uint32_t frange = static_cast<uint32_t>(TG - r0) * 4;
+    const __amdgpu_buffer_rsrc_t rf =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(src), static_cast<short>(0), static_cast<int>(frange),
+                                          kBufFlags);
+    lds_u8* const sdst = smem + opaque_s(LY::ST + r * LY::SB + wave * kBN * 4);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rf, (lds_void_t*)sdst, 4, static_cast<uint32_t>(lane) * 4, 0, 0, 0);
+  }
 }
 
-// One 64-row tile against the wave's 32 keys, as a two-block software pipeline:
-// the second block's score products are interleaved with the first block's
-// weights, and the first block's gradient products with the second block's
-// weights, so that the vector work runs while the matrix cores are busy.
-// qa holds the read addresses of stage buffer 0 and stat its base; the tile
-// sits B bytes further (a constant, carried in the instructions' offsets).
-template <int D, bool MASK, int B>
-__device__ __forceinline__ void kv_tile(f32x16 (&dka)[D / 32], f32x16 (&dva)[D / 32], const bf16x8 (&kf)[D / 16],
-                                        const bf16x8 (&vf)[D / 16], const TileReads<D>& qa, uint32_t stat0, int r0,
-                                        int lgG, int my_key, int half, float scale_log2) {
-  const uint32_t stat = stat0 + B;
-  constexpr int DO = RowStage<D>::DO - RowStage<D>::Q;
+// One row tile on the P side.  ta holds row-wise read addresses into stage 0's
+// Q tile and transposed ones into its dO tile; the tile's stage lies B bytes
+// further in both, its lse2 row S bytes past stat0 and its transfer slot X
+// bytes past xfer0 (all constants, so that every LDS address is a per-lane
+// offset plus an instruction immediate).
+template <int D, bool MASK, int B, int S, int X>
+__device__ __forceinline__ void p_tile(f32x16 (&acc)[D / 32], const bf16x8 (&kf)[D / 16], const TileReads<D>& ta,
+                                       uint32_t stat0, uint32_t xfer0, int r0, int lgG, int my_key, int half,
+                                       float scale_log2) {
   constexpr int NT = D / 32;
-  bf16x8 aq[D / 16], ao[D / 16];
-  f32x16 s0, dp0, s1, dp1;
-  f32x4 l2[4], dd[4];
-  bf16x8 tt[4 * NT];
-  bf16x8 pb0[2], db0[2], pb1[2], db1[2];
-  load_rows<D>(aq, ao, qa, B, DO);
-  kv_stats<D, 0>(stat, half, l2, dd);
-  __builtin_amdgcn_sched_barrier(0);
-  kv_scores<D>(aq, ao, kf, vf, s0, dp0);
-  load_rows<D>(aq, ao, qa, B + 32 * Tile<D>::ROW_BYTES, DO);
-  kv_fetch_tr<D, 0, B>(tt, qa);
-  __builtin_amdgcn_sched_barrier(0);
-  // region A: block 1's scores beside block 0's weights
-  kv_scores<D>(aq, ao, kf, vf, s1, dp1);
-  kv_weights<0, MASK>(s0, dp0, l2, dd, r0, lgG, my_key, half, scale_log2, pb0, db0);
-  interleave<D / 8, 6>();
-  __builtin_amdgcn_sched_barrier(0);
-  kv_stats<D, 1>(stat, half, l2, dd);
-  lds_ready(tt);
-  __builtin_amdgcn_sched_barrier(0);
-  // region B: block 0's gradient products beside block 1's weights
-  kv_accumulate<D>(dka, dva, tt, pb0, db0);
-  kv_weights<1, MASK>(s1, dp1, l2, dd, r0, lgG, my_key, half, scale_log2, pb1, db1);
-  interleave<4 * NT, 6>();
-  __builtin_amdgcn_sched_barrier(0);
-  kv_fetch_tr<D, 1, B>(tt, qa);
-  lds_ready(tt);
-  kv_accumulate<D>(dka, dva, tt, pb1, db1);
+  const uint32_t stat = stat0 + S, xfer = xfer0 + X;
+#pragma unroll
+  for (int J = 0; J < 2; ++J) {
+    bf16x8 aq[D / 16];
+#pragma unroll
+    for (int sl = 0; sl < D / 16; ++sl) aq[sl] = *lds_at<lds_bf16x8_t>(ta.nr[sl] + B + 32 * J * Tile<D>::ROW_BYTES);
+    f32x4 l2[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) l2[a] = *lds_at<lds_f32x4_t>(stat + (32 * J + 8 * a + 4 * half) * 4);
+    f32x16 sacc = {};
+#pragma unroll
+    for (int sl = 0; sl < D / 16; ++sl) sacc = mfma32(aq[sl], kf[sl], sacc);
+    bf16x8 tt[2 * NT];
+    if (J == 0)
+      fetch_tr_block<D, 0, B>(tt, ta);
+    else
+      fetch_tr_block<D, 1, B>(tt, ta);
+    float p[16];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        float x = fmaf(sacc[4 * a + c], scale_log2, -l2[a][c]);
+        if (MASK) x = my_key <= ((r0 + 32 * J + 8 * a + 4 * half + c) >> lgG) ? x : -INFINITY;
+        p[4 * a + c] = fast_exp2(x);
+      }
+    bf16x8 pb[2];
+    pack16(p, pb);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) *lds_at<lds_bf16x8_t>(xfer + (2 * J + h) * 1024) = pb[h];
+    lds_ready(tt);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int dt = 0; dt < NT; ++dt) acc[dt] = mfma32(tt[h * NT + dt], pb[h], acc[dt]);
+  }
 }
+
+// One row tile on the dS side.  ta holds row-wise read addresses into stage
+// 0's dO tile and transposed ones into its Q tile; B, S and X as in p_tile (S
+// addresses the tile's lse2 row, Dsum follows it).
+template <int D, int B, int S, int X>
+__device__ __forceinline__ void ds_tile(f32x16 (&acc)[D / 32], const bf16x8 (&vf)[D / 16], const TileReads<D>& ta,
+                                        uint32_t stat0, uint32_t xfer0, int half) {
+  constexpr int NT = D / 32;
+  const uint32_t stat = stat0 + S + kBN * 4, xfer = xfer0 + X;
+#pragma unroll
+  for (int J = 0; J < 2; ++J) {
+    bf16x8 ao[D / 16];
+#pragma unroll
+    for (int sl = 0; sl < D / 16; ++sl) ao[sl] = *lds_at<lds_bf16x8_t>(ta.nr[sl] + B + 32 * J * Tile<D>::ROW_BYTES);
+    f32x4 dd[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) dd[a] = *lds_at<lds_f32x4_t>(stat + (32 * J + 8 * a + 4 * half) * 4);
+    u32x4 pw[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) pw[h] = *lds_at<lds_u32x4_t>(xfer + (2 * J + h) * 1024);
+    f32x16 dp = {};
+#pragma unroll
+    for (int sl = 0; sl < D / 16; ++sl) dp = mfma32(ao[sl], vf[sl], dp);
+    bf16x8 tt[2 * NT];
+    if (J == 0)
+      fetch_tr_block<D, 0, B>(tt, ta);
+    else
+      fetch_tr_block<D, 1, B>(tt, ta);
+    float ds[16];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int i = 4 * a + c;
+        const uint32_t w = pw[i >> 3][(i & 7) >> 1];
+        const float pv = __builtin_bit_cast(float, (i & 1) ? (w & 0xffff0000u) : (w << 16));
+        ds[i] = pv * (dp[i] - dd[a][c]);
+      }
+    bf16x8 db[2];
+    pack16(ds, db);
+    lds_ready(tt);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int dt = 0; dt < NT; ++dt) acc[dt] = mfma32(tt[h * NT + dt], db[h], acc[dt]);
+  }
+}
+
+constexpr int kKvWaves = 8;
+constexpr int kKvThreads = kKvWaves * 64;
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))) void moda_bwd_dkv_kernel(
+__global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void moda_bwd_dkv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ ws_l2, const float* __restrict__ ws_dd, int B, int T,
     int Hq, int Hk, int lgG, float scale, float scale_log2, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
-  using RS = RowStage<D>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[2 * RS::BYTES];
+  using LY = RowStages<D>;
+  using XS = XferSlot<D>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[LY::BYTES];
   lds_u8* const smem = (lds_u8*)smem_raw;
 
   const int G = 1 << lgG;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool p_role = wave < 4;
+  const int pair = wave & 3;
   const int half = lane >> 5;
   const int nbh = B * Hk;
   const int kb = blockIdx.x / nbh;  // key block; causal: the heaviest (first) blocks go first
   const int bh = blockIdx.x % nbh;
   const int b = bh / Hk, hk = bh % Hk;
   const int k0 = kb * kKB;
-  const int kw0 = k0 + wave * 32;
+  const int kw0 = k0 + pair * 32;
   const int my_key = kw0 + (lane & 31);
   const int TG = T << lgG;
 
-  // K^T and V^T fragments (B operands): lane holds key my_key, d = 16*sl + 8*half + [0, 8).
+  // K^T (P wave) or V^T (dS wave) fragments: lane holds key my_key, d = 16*sl + 8*half + [0, 8).
   const int64_t koff = ((static_cast<int64_t>(b) * T + my_key) * Hk + hk) * D;
-  bf16x8 kf[D / 16], vf[D / 16];
+  const uint16_t* src = p_role ? k : v;
+  bf16x8 frag[D / 16];
 #pragma unroll
   for (int sl = 0; sl < D / 16; ++sl) {
-    u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
-    if (my_key < T) {
-      a = *reinterpret_cast<const u32x4*>(k + koff + sl * 16 + half * 8);
-      c = *reinterpret_cast<const u32x4*>(v + koff + sl * 16 + half * 8);
-    }
-    kf[sl] = __builtin_bit_cast(bf16x8, a);
-    vf[sl] = __builtin_bit_cast(bf16x8, c);
+    u32x4 a = {0u, 0u, 0u, 0u};
+    if (my_key < T) a = *reinterpret_cast<const u32x4*>(src + koff + sl * 16 + half * 8);
+    frag[sl] = __builtin_bit_cast(bf16x8, a);
   }
 
   const uint16_t* qb = q + (static_cast<int64_t>(b) * T * Hq + hk * G) * D;
@@ -784,71 +793,96 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
   const float* l2b = ws_l2 + (static_cast<int64_t>(b) * Hk + hk) * TG;
   const float* ddb = ws_dd + (static_cast<int64_t>(b) * Hk + hk) * TG;
   RowDma<D> dm;
-  init_row_dma<D>(dm, lane, wave, Hq, lgG);
+  init_row_dma<D>(dm, lane, pair, Hq, lgG);
   TileReads<D> ro;
   init_reads<D>(ro, lane);
 
-  f32x16 dka[D / 32], dva[D / 32];
+  f32x16 acc[D / 32];
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) {
-    dka[dt] = f32x16{};
-    dva[dt] = f32x16{};
-  }
+  for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
 
-  // Row tiles: causal rows see key j from token j on, so tiles start at the
-  // block's first key; those before token k0 + kKB - 1 need the mask.  The
-  // masked run is extended to an even length (the mask keeps every pair of an
-  // unmasked tile) so that both loops take tiles in pairs, the first of each
-  // pair in stage buffer 0: every LDS address is then a per-lane offset plus
-  // an instruction immediate.
   const int nt = (TG + kBN - 1) / kBN;
   const int i0 = CAUSAL ? (k0 << lgG) / kBN : 0;
-  const int i_m0 = CAUSAL ? min(nt, (((k0 + kKB - 1) << lgG) + kBN - 1) / kBN) : i0;
-  const int i_m = min(nt, i0 + ((i_m0 - i0 + 1) & ~1));
+  const int i_m = CAUSAL ? min(nt, (((k0 + kKB - 1) << lgG) + kBN - 1) / kBN) : i0;
   const uint32_t lds0 = lds_addr(smem);
-  const TileReads<D> ra = at<D>(ro, lds0 + RS::Q);  // stage buffer 0
+  // Stage-0 read addresses: the P side reads Q row-wise and dO transposed, the
+  // dS side dO row-wise and Q transposed.
+  TileReads<D> ra;
+  {
+    const uint32_t rowb = lds0 + (p_role ? LY::Q : LY::DO), trb = lds0 + (p_role ? LY::DO : LY::Q);
+#pragma unroll
+    for (int sl = 0; sl < D / 16; ++sl) ra.nr[sl] = rowb + ro.nr[sl];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      ra.lo[dt] = trb + ro.lo[dt];
+      ra.hi[dt] = trb + ro.hi[dt];
+    }
+  }
+  const uint32_t stat0 = lds0 + LY::ST;
+  const uint32_t xfer0 = lds0 + static_cast<uint32_t>(LY::XF + pair * XS::PAIR) + static_cast<uint32_t>(lane) * 16;
+  // No row of tile it sees the pair's keys.
+  auto skip = [&](int it) __attribute__((always_inline)) { return CAUSAL && ((it * kBN + kBN - 1) >> lgG) < kw0; };
 
-  // One tile in stage buffer P (the next one is loaded into buffer 1 - P).
-  auto tile = [&](auto parity, auto maskc, int it) __attribute__((always_inline)) {
-    constexpr int P = decltype(parity)::value;
+  // Step u (u = 0 .. nt - i0) publishes tile i0 + u, starts loading the next
+  // one, lets the P waves work on tile i0 + u and the dS waves on tile
+  // i0 + u - 1.  Tile i0 + u lives in stage and slot u % 3; the steps are
+  // unrolled by three so that the residue, and with it every LDS offset, is a
+  // constant.  The masked steps are rounded up to a multiple of three (the
+  // mask is exact on any tile, so the extra steps only cost a select).
+  using IC0 = std::integral_constant<int, 0>;
+  using IC1 = std::integral_constant<int, 1>;
+  using IC2 = std::integral_constant<int, 2>;
+  const int n_it = nt - i0 + 1;
+  const int n_mask = min(n_it, (i_m - i0 + 2) / 3 * 3);
+  auto p_step = [&](auto res, auto maskc, int u) __attribute__((always_inline)) {
+    constexpr int R = decltype(res)::value;
     constexpr bool MASK = decltype(maskc)::value != 0;
+    const int it = i0 + u;
     publish_tile();
-    if (it + 1 < nt)
-      dma_rows<D>(qb, ob, l2b, ddb, T, Hq, lgG, TG, it + 1, smem + opaque_s((1 - P) * RS::BYTES), wave, lane, dm);
-    const int r0 = it * kBN;
-    if (MASK && ((r0 + kBN - 1) >> lgG) < kw0) return;  // no row of this tile sees the wave's keys
-    kv_tile<D, MASK, P * RS::BYTES>(dka, dva, kf, vf, ra, lds0, r0, lgG, my_key, half, scale_log2);
+    if (it + 1 < nt) dma_rows<D>(qb, ob, l2b, ddb, T, Hq, lgG, TG, it + 1, smem, (R + 1) % 3, pair, lane, dm);
+    if (it >= nt || skip(it)) return;
+    p_tile<D, MASK, R * LY::TB, R * LY::SB, R * XS::BYTES>(acc, frag, ra, stat0, xfer0, it * kBN, lgG, my_key, half,
+                                                           scale_log2);
+  };
+  auto ds_step = [&](auto res, auto maskc, int u) __attribute__((always_inline)) {
+    constexpr int R = (decltype(res)::value + 2) % 3;  // the previous tile's stage and slot
+    publish_tile();
+    const int jt = i0 + u - 1;
+    if (u == 0 || skip(jt)) return;
+    ds_tile<D, R * LY::TB, R * LY::SB, R * XS::BYTES>(acc, frag, ra, stat0, xfer0, half);
+  };
+  // Steps [u, end) in threes, then at most two more (u % 3 == 0 on entry).
+  auto run = [&](auto step, auto maskc, int& u, int end) __attribute__((always_inline)) {
+    for (; u + 2 < end; u += 3) {
+      step(IC0(), maskc, u);
+      step(IC1(), maskc, u + 1);
+      step(IC2(), maskc, u + 2);
+    }
+    if (u < end) step(IC0(), maskc, u++);
+    if (u < end) step(IC1(), maskc, u++);
   };
 
-  int it = i0;
-  if (i0 < nt) dma_rows<D>(qb, ob, l2b, ddb, T, Hq, lgG, TG, i0, smem, wave, lane, dm);
-  for (; it + 1 < i_m; it += 2) {  // masked tiles (an even number of them, unless the rows run out)
-    tile(std::integral_constant<int, 0>(), std::integral_constant<int, 1>(), it);
-    tile(std::integral_constant<int, 1>(), std::integral_constant<int, 1>(), it + 1);
+  if (p_role && i0 < nt) dma_rows<D>(qb, ob, l2b, ddb, T, Hq, lgG, TG, i0, smem, 0, pair, lane, dm);
+  int u = 0;
+  if (p_role) {
+    run(p_step, IC1(), u, n_mask);
+    run(p_step, IC0(), u, n_it);
+  } else {
+    run(ds_step, IC1(), u, n_mask);
+    run(ds_step, IC0(), u, n_it);
   }
-  if (it < i_m) {  // only when i_m == nt
-    tile(std::integral_constant<int, 0>(), std::integral_constant<int, 1>(), it);
-    ++it;
-  }
-  for (; it + 1 < nt; it += 2) {  // unmasked tiles
-    tile(std::integral_constant<int, 0>(), std::integral_constant<int, 0>(), it);
-    tile(std::integral_constant<int, 1>(), std::integral_constant<int, 0>(), it + 1);
-  }
-  if (it < nt) tile(std::integral_constant<int, 0>(), std::integral_constant<int, 0>(), it);
 
   if (my_key < T) {
-    uint16_t* krow = dk + koff;
-    uint16_t* vrow = dv + koff;
+    uint16_t* row = (p_role ? dv : dk) + koff;
+    const float f = p_role ? 1.0f : scale;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const int d0 = dt * 32 + a * 8 + half * 4;
-        u32x2 wk = {pack_bf16x2(dka[dt][4 * a] * scale, dka[dt][4 * a + 1] * scale),
-                    pack_bf16x2(dka[dt][4 * a + 2] * scale, dka[dt][4 * a + 3] * scale)};
-        u32x2 wv = {pack_bf16x2(dva[dt][4 * a], dva[dt][4 * a + 1]), pack_bf16x2(dva[dt][4 * a + 2], dva[dt][4 * a + 3])};
-        *reinterpret_cast<u32x2*>(krow + d0) = wk;
-        *reinterpret_cast<u32x2*>(vrow + d0) = wv;
+        u32x2 w = {pack_bf16x2(acc[dt][4 * a] * f, acc[dt][4 * a + 1] * f),
+                   pack_bf16x2(acc[dt][4 * a + 2] * f, acc[dt][4 * a + 3] * f)};
+        *reinterpret_cast<u32x2*>(row + d0) = w;
       }
   }
 }
@@ -924,11 +958,11 @@ hipError_t launch_bwd_d(const BwdArgs& a) {
   const int nkb = (a.T + kKB - 1) / kKB;
   const unsigned kv_blocks = static_cast<unsigned>(static_cast<int64_t>(nkb) * a.B * a.Hk);
   if (a.causal)
-    hipLaunchKernelGGL((moda_bwd_dkv_kernel<D, true>), dim3(kv_blocks), dim3(kThreads), 0, st, q, k, v, dout, l2, dd,
+    hipLaunchKernelGGL((moda_bwd_dkv_kernel<D, true>), dim3(kv_blocks), dim3(kKvThreads), 0, st, q, k, v, dout, l2, dd,
                        a.B, a.T, a.Hq, a.Hk, lgG, scale, scale_log2, static_cast<uint16_t*>(a.dk),
                        static_cast<uint16_t*>(a.dv));
   else
-    hipLaunchKernelGGL((moda_bwd_dkv_kernel<D, false>), dim3(kv_blocks), dim3(kThreads), 0, st, q, k, v, dout, l2, dd,
+    hipLaunchKernelGGL((moda_bwd_dkv_kernel<D, false>), dim3(kv_blocks), dim3(kKvThreads), 0, st, q, k, v, dout, l2, dd,
                        a.B, a.T, a.Hq, a.Hk, lgG, scale, scale_log2, static_cast<uint16_t*>(a.dk),
                        static_cast<uint16_t*>(a.dv));
   return hipGetLastError();
