@@ -654,7 +654,41 @@ __device__ __forceinline__ void dma_rows(const uint16_t* qb, const uint16_t* ob,
   }
 }
 
-// One row tile on the P side.  ta holds row-wise read addresses into stage 0's
+// P of one 32-row block from its scores: exp2(s * scale * log2e - lse2), masked.
+template <int J, bool MASK>
+__device__ __forceinline__ void p_weights(const f32x16& s, const f32x4 (&l2)[4], int r0, int lgG, int my_key,
+                                          int half, float scale_log2, bf16x8 (&pb)[2]) {
+  float p[16];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      float x = fmaf(s[4 * a + c], scale_log2, -l2[a][c]);
+      if (MASK) x = my_key <= ((r0 + 32 * J + 8 * a + 4 * half + c) >> lgG) ? x : -INFINITY;
+      p[4 * a + c] = fast_exp2(x);
+    }
+  pack16(p, pb);
+}
+
+// dS = P (dP - Dsum) of one 32-row block, P as the P wave stored it (bf16).
+__device__ __forceinline__ void ds_weights(const f32x16& dp, const f32x4 (&dd)[4], const u32x4 (&pw)[2],
+                                           bf16x8 (&db)[2]) {
+  float ds[16];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int i = 4 * a + c;
+      const uint32_t w = pw[i >> 3][(i & 7) >> 1];
+      const float pv = __builtin_bit_cast(float, (i & 1) ? (w & 0xffff0000u) : (w << 16));
+      ds[i] = pv * (dp[i] - dd[a][c]);
+    }
+  pack16(ds, db);
+}
+
+// One row tile on the P side, its two 32-row blocks as a software pipeline:
+// block 1's score products run beside block 0's weights, block 0's dV products
+// beside block 1's weights.  ta holds row-wise read addresses into stage 0's
 // Q tile and transposed ones into its dO tile; the tile's stage lies B bytes
 // further in both, its lse2 row S bytes past stat0 and its transfer slot X
 // bytes past xfer0 (all constants, so that every LDS address is a per-lane
@@ -664,89 +698,100 @@ __device__ __forceinline__ void p_tile(f32x16 (&acc)[D / 32], const bf16x8 (&kf)
                                        uint32_t stat0, uint32_t xfer0, int r0, int lgG, int my_key, int half,
                                        float scale_log2) {
   constexpr int NT = D / 32;
+  constexpr int RB = Tile<D>::ROW_BYTES;
   const uint32_t stat = stat0 + S, xfer = xfer0 + X;
+  bf16x8 aq[D / 16], tt[2 * NT], pb0[2], pb1[2];
+  f32x4 l2[4];
 #pragma unroll
-  for (int J = 0; J < 2; ++J) {
-    bf16x8 aq[D / 16];
+  for (int sl = 0; sl < D / 16; ++sl) aq[sl] = *lds_at<lds_bf16x8_t>(ta.nr[sl] + B);
 #pragma unroll
-    for (int sl = 0; sl < D / 16; ++sl) aq[sl] = *lds_at<lds_bf16x8_t>(ta.nr[sl] + B + 32 * J * Tile<D>::ROW_BYTES);
-    f32x4 l2[4];
+  for (int a = 0; a < 4; ++a) l2[a] = *lds_at<lds_f32x4_t>(stat + (8 * a + 4 * half) * 4);
+  __builtin_amdgcn_sched_barrier(0);
+  f32x16 s0 = {}, s1 = {};
 #pragma unroll
-    for (int a = 0; a < 4; ++a) l2[a] = *lds_at<lds_f32x4_t>(stat + (32 * J + 8 * a + 4 * half) * 4);
-    f32x16 sacc = {};
+  for (int sl = 0; sl < D / 16; ++sl) s0 = mfma32(aq[sl], kf[sl], s0);
 #pragma unroll
-    for (int sl = 0; sl < D / 16; ++sl) sacc = mfma32(aq[sl], kf[sl], sacc);
-    bf16x8 tt[2 * NT];
-    if (J == 0)
-      fetch_tr_block<D, 0, B>(tt, ta);
-    else
-      fetch_tr_block<D, 1, B>(tt, ta);
-    float p[16];
+  for (int sl = 0; sl < D / 16; ++sl) aq[sl] = *lds_at<lds_bf16x8_t>(ta.nr[sl] + B + 32 * RB);
+  fetch_tr_block<D, 0, B>(tt, ta);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+  for (int sl = 0; sl < D / 16; ++sl) s1 = mfma32(aq[sl], kf[sl], s1);
+  p_weights<0, MASK>(s0, l2, r0, lgG, my_key, half, scale_log2, pb0);
+  interleave<D / 16, MASK ? 8 : 5>();
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        float x = fmaf(sacc[4 * a + c], scale_log2, -l2[a][c]);
-        if (MASK) x = my_key <= ((r0 + 32 * J + 8 * a + 4 * half + c) >> lgG) ? x : -INFINITY;
-        p[4 * a + c] = fast_exp2(x);
-      }
-    bf16x8 pb[2];
-    pack16(p, pb);
+  for (int h = 0; h < 2; ++h) *lds_at<lds_bf16x8_t>(xfer + h * 1024) = pb0[h];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) *lds_at<lds_bf16x8_t>(xfer + (2 * J + h) * 1024) = pb[h];
-    lds_ready(tt);
+  for (int a = 0; a < 4; ++a) l2[a] = *lds_at<lds_f32x4_t>(stat + (32 + 8 * a + 4 * half) * 4);
+  lds_ready(tt);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+  for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int dt = 0; dt < NT; ++dt) acc[dt] = mfma32(tt[h * NT + dt], pb[h], acc[dt]);
-  }
+    for (int dt = 0; dt < NT; ++dt) acc[dt] = mfma32(tt[h * NT + dt], pb0[h], acc[dt]);
+  p_weights<1, MASK>(s1, l2, r0, lgG, my_key, half, scale_log2, pb1);
+  interleave<2 * NT, MASK ? 8 : 5>();
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) *lds_at<lds_bf16x8_t>(xfer + (2 + h) * 1024) = pb1[h];
+  fetch_tr_block<D, 1, B>(tt, ta);
+  lds_ready(tt);
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int dt = 0; dt < NT; ++dt) acc[dt] = mfma32(tt[h * NT + dt], pb1[h], acc[dt]);
 }
 
-// One row tile on the dS side.  ta holds row-wise read addresses into stage
-// 0's dO tile and transposed ones into its Q tile; B, S and X as in p_tile (S
-// addresses the tile's lse2 row, Dsum follows it).
+// One row tile on the dS side, pipelined like p_tile.  ta holds row-wise read
+// addresses into stage 0's dO tile and transposed ones into its Q tile; B, S
+// and X as in p_tile (S addresses the tile's lse2 row, Dsum follows it).
 template <int D, int B, int S, int X>
 __device__ __forceinline__ void ds_tile(f32x16 (&acc)[D / 32], const bf16x8 (&vf)[D / 16], const TileReads<D>& ta,
                                         uint32_t stat0, uint32_t xfer0, int half) {
   constexpr int NT = D / 32;
+  constexpr int RB = Tile<D>::ROW_BYTES;
   const uint32_t stat = stat0 + S + kBN * 4, xfer = xfer0 + X;
+  bf16x8 ao[D / 16], tt[2 * NT], db0[2], db1[2];
+  f32x4 dd[4];
+  u32x4 pw[2];
 #pragma unroll
-  for (int J = 0; J < 2; ++J) {
-    bf16x8 ao[D / 16];
+  for (int sl = 0; sl < D / 16; ++sl) ao[sl] = *lds_at<lds_bf16x8_t>(ta.nr[sl] + B);
 #pragma unroll
-    for (int sl = 0; sl < D / 16; ++sl) ao[sl] = *lds_at<lds_bf16x8_t>(ta.nr[sl] + B + 32 * J * Tile<D>::ROW_BYTES);
-    f32x4 dd[4];
+  for (int a = 0; a < 4; ++a) dd[a] = *lds_at<lds_f32x4_t>(stat + (8 * a + 4 * half) * 4);
 #pragma unroll
-    for (int a = 0; a < 4; ++a) dd[a] = *lds_at<lds_f32x4_t>(stat + (32 * J + 8 * a + 4 * half) * 4);
-    u32x4 pw[2];
+  for (int h = 0; h < 2; ++h) pw[h] = *lds_at<lds_u32x4_t>(xfer + h * 1024);
+  __builtin_amdgcn_sched_barrier(0);
+  f32x16 dp0 = {}, dp1 = {};
 #pragma unroll
-    for (int h = 0; h < 2; ++h) pw[h] = *lds_at<lds_u32x4_t>(xfer + (2 * J + h) * 1024);
-    f32x16 dp = {};
+  for (int sl = 0; sl < D / 16; ++sl) dp0 = mfma32(ao[sl], vf[sl], dp0);
 #pragma unroll
-    for (int sl = 0; sl < D / 16; ++sl) dp = mfma32(ao[sl], vf[sl], dp);
-    bf16x8 tt[2 * NT];
-    if (J == 0)
-      fetch_tr_block<D, 0, B>(tt, ta);
-    else
-      fetch_tr_block<D, 1, B>(tt, ta);
-    float ds[16];
+  for (int sl = 0; sl < D / 16; ++sl) ao[sl] = *lds_at<lds_bf16x8_t>(ta.nr[sl] + B + 32 * RB);
+  fetch_tr_block<D, 0, B>(tt, ta);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+  for (int sl = 0; sl < D / 16; ++sl) dp1 = mfma32(ao[sl], vf[sl], dp1);
+  ds_weights(dp0, dd, pw, db0);
+  interleave<D / 16, 7>();
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int i = 4 * a + c;
-        const uint32_t w = pw[i >> 3][(i & 7) >> 1];
-        const float pv = __builtin_bit_cast(float, (i & 1) ? (w & 0xffff0000u) : (w << 16));
-        ds[i] = pv * (dp[i] - dd[a][c]);
-      }
-    bf16x8 db[2];
-    pack16(ds, db);
-    lds_ready(tt);
+  for (int a = 0; a < 4; ++a) dd[a] = *lds_at<lds_f32x4_t>(stat + (32 + 8 * a + 4 * half) * 4);
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+  for (int h = 0; h < 2; ++h) pw[h] = *lds_at<lds_u32x4_t>(xfer + (2 + h) * 1024);
+  lds_ready(tt);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int dt = 0; dt < NT; ++dt) acc[dt] = mfma32(tt[h * NT + dt], db[h], acc[dt]);
-  }
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int dt = 0; dt < NT; ++dt) acc[dt] = mfma32(tt[h * NT + dt], db0[h], acc[dt]);
+  ds_weights(dp1, dd, pw, db1);
+  interleave<2 * NT, 7>();
+  __builtin_amdgcn_sched_barrier(0);
+  fetch_tr_block<D, 1, B>(tt, ta);
+  lds_ready(tt);
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int dt = 0; dt < NT; ++dt) acc[dt] = mfma32(tt[h * NT + dt], db1[h], acc[dt]);
 }
 
 constexpr int kKvWaves = 8;
