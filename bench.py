@@ -414,6 +414,71 @@ def depth_write_leg(kd, vd, iters=10):
                          "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
 
 
+def workloads_leg(iters=8):
+    """Forward timings at the other benchmark workloads of the pages' kernel study: the
+    700M-class layer, the depth sweep (L = 0, 12, 48, 96) and the GQA group sweep (G = 1..8,
+    keys x 0.5).  Each L > 0 shape is timed against an L=0 forward on the same q / k_seq /
+    v_seq (calls interleaved, median of HIP-event times after one warm-up call each); inputs
+    are drawn on the GPU from each workload's seeds, depth packed once before timing.  The
+    depth sweep also gives the marginal depth-stream rate: the slope of time against depth
+    bytes over its four points."""
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    rows = []
+    sweep = []  # (depth bytes, ms) of the depth sweep
+    cases = [(2, 0)] + [(3, v) for v in range(4)] + [(4, v) for v in range(4)]
+    for c, v in cases:
+        shape = I.workload(c, v)
+        dev = I.workload_inputs(c, v, device="cuda")
+        kd = api.moda_pack_depth(dev.pop("k_depth")) if shape.L else None
+        vd = api.moda_pack_depth(dev.pop("v_depth")) if shape.L else None
+        dev.pop("k_depth", None), dev.pop("v_depth", None)
+        out = torch.empty_like(dev["q"])
+        lse = torch.empty((shape.B, shape.Hq, shape.T), dtype=torch.float32, device="cuda")
+        out0, lse0 = torch.empty_like(out), torch.empty_like(lse)
+
+        def run():
+            api.moda_attn_fwd(dev["q"], dev["k_seq"], dev["v_seq"], kd, vd, causal=True, out=out, lse=lse)
+
+        def run0():
+            api.moda_attn_fwd(dev["q"], dev["k_seq"], dev["v_seq"], None, None, causal=True, out=out0, lse=lse0)
+
+        run(), run0()
+        t, t0 = [], []
+        for _ in range(iters):
+            t.append(timed(run))
+            t0.append(timed(run0))
+        ms, ms0 = float(np.median(t)), float(np.median(t0))
+        F = acc.flops(shape)
+        Fseq = acc.flops_seq(shape.B, shape.T, shape.Hq, shape.d)
+        row = {"workload": c, "shape": shape.describe(), "ms": round(ms, 4), "l0_ms": round(ms0, 4),
+               "ratio_vs_l0": round(ms / ms0, 4), "tflops": round(F / (ms * 1e-3) / 1e12, 1),
+               "seq_mfma_util": round(Fseq / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+               "depth_gb": round(acc.depth_bytes(shape) / 1e9, 3)}
+        if shape.L:
+            row["depth_marginal_gbs"] = round(acc.depth_bytes(shape) / max(1e-9, (ms - ms0) * 1e-3) / 1e9, 1)
+        rows.append(row)
+        if c == 3:
+            sweep.append((acc.depth_bytes(shape), ms))
+        del dev, kd, vd, out, lse, out0, lse0
+        torch.cuda.empty_cache()
+    x = np.array([b for b, _ in sweep], dtype=np.float64)
+    y = np.array([m for _, m in sweep], dtype=np.float64) * 1e-3
+    slope = np.polyfit(x, y, 1)[0]  # seconds per depth byte
+    return {"rows": rows,
+            "depth_sweep_marginal_gbs": round(1.0 / slope / 1e9, 1) if slope > 0 else None,
+            "note": "each ratio is against an L=0 forward on the same sequence inputs; depth_marginal_gbs = "
+                    "depth bytes / (t - t_L0); the sweep figure is the slope of t over depth bytes, L=0..96"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -424,6 +489,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
     ap.add_argument("--no-depth-write", action="store_true", help="skip the depth-write (KV projection) measurement")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the forward timings at the 700M-class, depth-sweep and GQA-sweep workloads")
     ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write the profiles/ summary from rocprofv3 CSV output directories and exit")
     ap.add_argument("--sq", metavar="SQ_DIR", nargs="+", help="with --summarize: also summarise SQ counter passes")
@@ -518,6 +585,8 @@ def main():
         rec["decode"] = decode_leg()
     if not args.no_depth_write:  # last: it overwrites the final depth slot of the step's buffers
         rec["depth_write"] = depth_write_leg(kd, vd)
+    if not args.no_workloads:
+        rec["workloads"] = workloads_leg()
     if not args.no_cpu_baseline:
         host = {k: v.cpu() for k, v in dev.items()}
         cpu, rows, ref = cpu_baseline(shape, host, args.cpu_seconds)
