@@ -479,6 +479,53 @@ def workloads_leg(iters=8):
                     "depth bytes / (t - t_L0); the sweep figure is the slope of t over depth bytes, L=0..96"}
 
 
+def table2_leg(iters=5):
+    """Forward-only timings at the shape of the pages' kernel table (B=1, d=64, G=8, Hq=64,
+    Hk=8, L=64, causal; T from 4096 to 65536), each against an L=0 forward on the same
+    sequence inputs.  The pages time forward + backward of Triton kernels on another GPU,
+    so only the trend of the extra time with T is comparable; both conventions are given:
+    (t - t0) / t as in the pages' table and (t - t0) / t0."""
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    rows = []
+    for T in (4096, 8192, 16384, 32768, 65536):
+        shape = I.Shape(1, T, 64, 8, 64, 64)
+        dev = I.make_inputs(shape, {n: 8000 + k for k, n in enumerate(I.TENSORS)}, device="cuda")
+        kd = api.moda_pack_depth(dev.pop("k_depth"))
+        vd = api.moda_pack_depth(dev.pop("v_depth"))
+        out = torch.empty_like(dev["q"])
+        lse = torch.empty((1, shape.Hq, T), dtype=torch.float32, device="cuda")
+
+        def run():
+            api.moda_attn_fwd(dev["q"], dev["k_seq"], dev["v_seq"], kd, vd, causal=True, out=out, lse=lse)
+
+        def run0():
+            api.moda_attn_fwd(dev["q"], dev["k_seq"], dev["v_seq"], None, None, causal=True, out=out, lse=lse)
+
+        run(), run0()
+        t, t0 = [], []
+        for _ in range(iters):
+            t.append(timed(run))
+            t0.append(timed(run0))
+        ms, ms0 = float(np.median(t)), float(np.median(t0))
+        rows.append({"T": T, "ms": round(ms, 4), "l0_ms": round(ms0, 4),
+                     "extra_over_t": round((ms - ms0) / ms, 4), "extra_over_t0": round((ms - ms0) / ms0, 4),
+                     "time_ratio_l0_over_moda": round(ms0 / ms, 4),
+                     "tflops": round(acc.flops(shape) / (ms * 1e-3) / 1e12, 1)})
+        del dev, kd, vd, out, lse
+        torch.cuda.empty_cache()
+    return {"workload": "forward at the pages' kernel-table shape B=1 d=64 G=8 Hq=64 Hk=8 L=64 causal, "
+                        "T=4096..65536, each against L=0 on the same inputs", "rows": rows}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -489,6 +536,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
     ap.add_argument("--no-depth-write", action="store_true", help="skip the depth-write (KV projection) measurement")
+    ap.add_argument("--table2", action="store_true",
+                    help="only time the forward at the pages' kernel-table shape over T and print that JSON line")
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the forward timings at the 700M-class, depth-sweep and GQA-sweep workloads")
     ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
@@ -509,6 +558,9 @@ def main():
         sys.exit(2)
     _lib.ensure_built()
     torch.cuda.set_device(0)
+    if args.table2:
+        print(json.dumps(table2_leg()), flush=True)
+        return
 
     shape = I.workload(5, 0)
     shape0 = I.workload(5, 1)
