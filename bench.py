@@ -40,10 +40,14 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "moda_fwd_bf16_long_L48_traffic.js
 
 
 def kernel_source_hash():
+    """Hash of the forward kernel's sources and its build flags (the counters describe one binary)."""
+    from depth_stream_attention_amd import build as pkg_build
     h = hashlib.sha256()
     for name in ("moda_fwd_bf16.hip", "moda_tile.h", "moda_device.h"):
         with open(os.path.join(ROOT, "depth_stream_attention_amd", "csrc", name), "rb") as f:
             h.update(f.read())
+    flags = [f for f in pkg_build.HIPCC_FLAGS if not f.startswith("-I")]  # include paths vary by checkout
+    h.update(" ".join(flags + pkg_build.SOURCE_FLAGS.get("moda_fwd_bf16.hip", [])).encode())
     return h.hexdigest()[:16]
 
 
