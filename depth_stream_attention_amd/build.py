@@ -15,12 +15,14 @@ SOURCES = ["moda_api.cpp", "moda_fwd_bf16.hip", "moda_fwd_f32.hip", "moda_pack.h
 
 # Per-source extra flags.  The bf16 kernels never produce NaN from finite
 # inputs, and without NaN semantics each fmaxf in their row-max chains needs no
-# canonicalising v_max_f32 x, x before the v_max3_f32.  The forward is
-# scheduled with the iterative ILP strategy: same registers, no spills,
-# bit-identical results, 1.7% faster at the long-context L=48 workload
-# (16.05 vs 16.33 ms, 15 interleaved runs; L=0 unchanged).
-SOURCE_FLAGS = {"moda_fwd_bf16.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
-                "moda_decode.hip": ["-fno-honor-nans"], "moda_bwd.hip": ["-fno-honor-nans"]}
+# canonicalising v_max_f32 x, x before the v_max3_f32.  The forward, backward
+# and KV projection are scheduled with the iterative ILP strategy (no spills,
+# bit-identical forward results): forward 1.7% faster at the long-context L=48
+# workload (16.05 vs 16.33 ms, 15 interleaved runs), backward about 1% faster,
+# the KV projection 2-5%; the decode kernels gained nothing and keep the default.
+_ILP = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
+SOURCE_FLAGS = {"moda_fwd_bf16.hip": ["-fno-honor-nans"] + _ILP, "moda_decode.hip": ["-fno-honor-nans"],
+                "moda_bwd.hip": ["-fno-honor-nans"] + _ILP, "moda_kvproj.hip": _ILP}
 
 # Packed-fp32 VALU forms are switched off for all device code.
 HIPCC_FLAGS = [
