@@ -8,8 +8,12 @@ from .api import (  # noqa: F401
     moda_append_depth_slot,
     moda_attn_bwd,
     moda_attn_bwd_workspace,
+    moda_attn_decode,
+    moda_attn_decode_ring,
+    moda_attn_decode_workspace,
     moda_attn_fwd,
     moda_attn_fwd_f32,
+    moda_attn_fwd_ring,
     moda_block_span,
     moda_error_string,
     moda_kv_project,

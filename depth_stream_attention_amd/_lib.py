@@ -6,15 +6,36 @@ import re
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmoda.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "moda.h")
+PROBE_LIB_PATH = os.path.join(PKG, "libmoda_probe.so")
+PROBE_HEADER = os.path.join(os.path.dirname(PKG), "include", "moda_probe.h")
 
 _lib = None
+_probe = None
 
 
-def declared_symbols():
-    """Names of the functions include/moda.h declares."""
-    text = open(HEADER).read()
+def declared_symbols(header=HEADER):
+    """Names of the functions a header (include/moda.h by default) declares."""
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(moda_[a-z0-9_]+)\s*\(", text)))
+
+
+def load_probe():
+    """Load libmoda_probe.so, the measurement kernels of include/moda_probe.h."""
+    global _probe
+    if _probe is not None:
+        return _probe
+    if not os.path.exists(PROBE_LIB_PATH):
+        raise RuntimeError("libmoda_probe.so is not built (%s)" % PROBE_LIB_PATH)
+    lib = ctypes.CDLL(PROBE_LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.moda_probe_mfma_bf16.argtypes = [vp, i32, i32, vp]
+    lib.moda_probe_copy.argtypes = [vp, vp, sz, i32, vp]
+    lib.moda_probe_read.argtypes = [vp, sz, i32, vp, vp]
+    for fn in (lib.moda_probe_mfma_bf16, lib.moda_probe_copy, lib.moda_probe_read):
+        fn.restype = i32
+    _probe = lib
+    return lib
 
 
 def load():
@@ -60,7 +81,7 @@ def load():
 
 def ensure_built():
     """Load the library, compiling it first only if no built copy exists."""
-    if not os.path.exists(LIB_PATH):
+    if not os.path.exists(LIB_PATH) or not os.path.exists(PROBE_LIB_PATH):
         from . import build
         build.build()
     return load()

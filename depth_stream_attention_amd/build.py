@@ -9,6 +9,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoda.so")
+# Measurement kernels (include/moda_probe.h): a library of their own, not part of libmoda.so.
+PROBE_LIB = os.path.join(PKG, "libmoda_probe.so")
+PROBE_SOURCES = ["moda_probe.hip"]
 BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["moda_api.cpp", "moda_fwd_bf16.hip", "moda_fwd_f32.hip", "moda_pack.hip", "moda_decode.hip",
            "moda_bwd.hip", "moda_kvproj.hip"]
@@ -40,7 +43,8 @@ def _hipcc():
 
 
 def build(verbose: bool = False, extra_flags=()) -> str:
-    """Compile every source for gfx950 and link libmoda.so next to this file."""
+    """Compile every source for gfx950 and link libmoda.so (and the measurement library
+    libmoda_probe.so) next to this file."""
     hipcc = _hipcc()
     os.makedirs(BUILD_DIR, exist_ok=True)
 
@@ -61,13 +65,14 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         return obj
 
     with ThreadPoolExecutor(max_workers=4) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True, capture_output=not verbose)
-    os.replace(tmp, LIB)
+        objs = list(ex.map(compile_one, SOURCES + PROBE_SOURCES))
+    for lib, lib_objs in ((LIB, objs[:len(SOURCES)]), (PROBE_LIB, objs[len(SOURCES):])):
+        tmp = lib + ".tmp%d" % os.getpid()
+        cmd = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + lib_objs
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True, capture_output=not verbose)
+        os.replace(tmp, lib)
     return LIB
 
 

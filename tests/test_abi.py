@@ -200,3 +200,25 @@ def test_kv_project_validation(lib):
         assert kvp(lib, **kw) == api.MODA_ERR_UNSUPPORTED, kw
     for name in ("x", "w", "ko", "vo", "kd", "vd"):
         assert kvp(lib, **{name: MIS}) == api.MODA_ERR_ALIGN, name
+
+
+def test_probe_library_exports_and_validates():
+    # the measurement kernels' library: every declared symbol, and host-side argument checks
+    probe = _lib.load_probe()
+    names = _lib.declared_symbols(_lib.PROBE_HEADER)
+    assert {"moda_probe_mfma_bf16", "moda_probe_copy", "moda_probe_read"} <= set(names)
+    for n in names:
+        assert hasattr(probe, n), "libmoda_probe.so does not export %s" % n
+    null = ctypes.c_void_p(0)
+    assert probe.moda_probe_mfma_bf16(null, 4, 4, None) == api.MODA_ERR_NULL
+    assert probe.moda_probe_mfma_bf16(A, 0, 4, None) == api.MODA_ERR_SHAPE
+    assert probe.moda_probe_mfma_bf16(A, 4, 0, None) == api.MODA_ERR_SHAPE
+    assert probe.moda_probe_mfma_bf16(MIS, 4, 4, None) == api.MODA_ERR_ALIGN
+    assert probe.moda_probe_copy(null, A2, 64, 4, None) == api.MODA_ERR_NULL
+    assert probe.moda_probe_copy(A, A2, 63, 4, None) == api.MODA_ERR_SHAPE
+    assert probe.moda_probe_copy(A, A2, 0, 4, None) == api.MODA_ERR_SHAPE
+    assert probe.moda_probe_copy(A, A2, 64, 0, None) == api.MODA_ERR_SHAPE
+    assert probe.moda_probe_copy(A, MIS, 64, 4, None) == api.MODA_ERR_ALIGN
+    assert probe.moda_probe_read(A, 64, 4, null, None) == api.MODA_ERR_NULL
+    assert probe.moda_probe_read(A, 40, 4, A2, None) == api.MODA_ERR_SHAPE
+    assert probe.moda_probe_read(MIS, 64, 4, A2, None) == api.MODA_ERR_ALIGN

@@ -1,11 +1,13 @@
 """The five workloads at full size, in the launch configuration the benchmark times,
 checked on stratified sampled rows against the oracle (rows are independent, so each
 sampled row is an exact check), plus finiteness of every output element."""
+import numpy as np
 import pytest
 import torch
 
+import oracle
 from depth_stream_attention_amd import inputs as I
-from parity_util import full_parity, run_path, sample_rows, sampled_parity, say
+from parity_util import BF16_MAX, check, full_parity, run_path, sample_rows, sampled_parity, say
 
 pytestmark = pytest.mark.gpu
 
@@ -44,3 +46,61 @@ def test_workload4(v):
 @pytest.mark.parametrize("v", [0, 1])
 def test_workload5(v):
     _run(5, v, n_uniform=16)
+
+
+def _late_rows(shape, seed, n_uniform=16):
+    """Rows (b, t, h) weighted to the end of the sequence: t in {T-2, T-1}, both edges of
+    each of the last eight 128-row query blocks, the first two tokens, and seeded-uniform
+    tokens, for every (b, h)."""
+    T, G = shape.T, shape.G
+    tb = max(1, 128 // G)
+    special = {0, 1, T - 2, T - 1}
+    for i in range(8):
+        special |= {T - (i + 1) * tb, T - i * tb - 1}
+    rng = np.random.default_rng(seed)
+    rows = []
+    for b in range(shape.B):
+        for h in range(shape.Hq):
+            ts = {t for t in special if 0 <= t < T} | set(rng.integers(0, T, n_uniform).tolist())
+            rows += [(b, t, h) for t in sorted(ts)]
+    return np.array(rows, dtype=np.int32)
+
+
+@pytest.mark.parametrize("c,v", [(5, 0), (3, 3)])
+def test_depth_aligned_full_size(c, v):
+    """Depth-aligned stress at full size (the long-context workload, L=48, and the depth
+    sweep's L=96).  Each depth key of (b, t, hk) is the query of head hk*G plus 0.5 times
+    noise, so that head's depth logits sit near sqrt(d) and its depth slots carry most of
+    its softmax mass at every position, including t = T-1; with N(0,1) inputs depth holds
+    only about L/(t+1+L) of the mass there (equal-logit case of the joint softmax: MoDA
+    reading notes, 二.2 worked example), which the tolerances alone would hide.  The test
+    also shows that it can see a depth indexing mistake: the oracle's result for the same
+    rows with every token given the previous token's depth slab must differ from the true
+    result, on every lead-head row, by far more than the tolerance."""
+    shape = I.workload(c, v)
+    say("depth-aligned workload", c, "variant", v, shape.describe())
+    dev = I.workload_inputs(c, v, depth_aligned=True, device="cuda")
+    out, lse = run_path(shape, dev)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    rows = _late_rows(shape, seed=500 + 10 * c + v)
+    host = {k: t.cpu() for k, t in dev.items()}
+    del dev
+    torch.cuda.empty_cache()
+    ref_out, ref_lse = oracle.moda_fwd_rows(host["q"], host["k_seq"], host["v_seq"], host["k_depth"],
+                                            host["v_depth"], rows, causal=shape.causal)
+    b, t, h = (torch.from_numpy(rows[:, i].astype(np.int64)).cuda() for i in range(3))
+    check(shape, out[b, t, h].float().cpu().numpy(), lse[b, h, t].cpu().numpy(), ref_out, ref_lse,
+          "depth-aligned %d.%d" % (c, v))
+    del out, lse
+    torch.cuda.empty_cache()
+
+    # Sensitivity: token t reads token t-1's depth slab (token 0 reads the last token's).
+    lead = (rows[:, 2] % shape.G == 0) & (rows[:, 1] >= 1)
+    kd_prev = torch.roll(host["k_depth"], 1, dims=1)
+    vd_prev = torch.roll(host["v_depth"], 1, dims=1)
+    bad_out, _ = oracle.moda_fwd_rows(host["q"], host["k_seq"], host["v_seq"], kd_prev, vd_prev, rows[lead],
+                                      causal=shape.causal)
+    gap = np.abs(bad_out - ref_out[lead]).max(axis=1)
+    say("depth-aligned %d.%d: previous-slab mistake moves lead-head rows by %.3g .. %.3g (n=%d)"
+        % (c, v, gap.min(), gap.max(), gap.size))
+    assert gap.size > 0 and gap.min() > 10 * BF16_MAX, "the stress input does not expose a wrong depth slab"
