@@ -9,6 +9,7 @@ from .api import (  # noqa: F401
     moda_attn_bwd,
     moda_attn_bwd_workspace,
     moda_attn_decode,
+    moda_attn_decode_noalloc,
     moda_attn_decode_ring,
     moda_attn_decode_workspace,
     moda_attn_fwd,

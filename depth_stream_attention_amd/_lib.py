@@ -59,6 +59,8 @@ def load():
     lib.moda_attn_decode_ring.restype = i32
     lib.moda_attn_decode.argtypes = [vp] * 5 + [i32] * 6 + [vp, vp, vp, ctypes.c_size_t, vp]
     lib.moda_attn_decode.restype = i32
+    lib.moda_attn_decode_noalloc.argtypes = [vp] * 5 + [i32] * 6 + [vp, vp, vp]
+    lib.moda_attn_decode_noalloc.restype = i32
     lib.moda_attn_bwd.argtypes = [vp] * 8 + [i32] * 7 + [vp] * 6 + [ctypes.c_size_t, vp]
     lib.moda_attn_bwd.restype = i32
     lib.moda_attn_bwd_workspace.argtypes = [i32] * 6

@@ -19,6 +19,8 @@ MODA_ERR_SHAPE = -2
 MODA_ERR_UNSUPPORTED = -3
 MODA_ERR_ALIGN = -4
 MODA_ERR_HIP = -5
+MODA_ERR_TOO_LARGE = -6
+MODA_DECODE_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class MODAError(RuntimeError):
@@ -232,6 +234,41 @@ def moda_attn_decode(q, k_cache, v_cache, k_depth=None, v_depth=None, out=None, 
                                   workspace.numel(), _stream(stream))
     if rc != MODA_OK:
         raise MODAError("moda_attn_decode_ring" if ring_L is not None else "moda_attn_decode", rc)
+    return out, lse
+
+
+def moda_attn_decode_noalloc(q, k_cache, v_cache, k_depth, v_depth, out, lse, stream=None):
+    """moda_attn_decode with no workspace: the library keeps the partial results in its fixed
+    per-GPU scratch (MODA_DECODE_NOALLOC_SCRATCH_BYTES), so the call allocates nothing.  out
+    [B,Hq,d] bf16 and lse [B,Hq] fp32 are the caller's; other arguments as moda_attn_decode
+    (k_depth, v_depth None for L = 0).  Calls that overlap in time on one GPU race on the
+    scratch.  Returns (out, lse)."""
+    dtype = torch.bfloat16
+    _check(q, "q", dtype, 3)
+    _check(k_cache, "k_cache", dtype, 4)
+    _check(v_cache, "v_cache", dtype, 4)
+    B, Hq, d = q.shape
+    T, Hk = k_cache.shape[1], k_cache.shape[2]
+    if tuple(k_cache.shape) != (B, T, Hk, d) or tuple(v_cache.shape) != (B, T, Hk, d):
+        raise ValueError("k_cache / v_cache must be [B,T,Hk,d] = %s" % ((B, T, Hk, d),))
+    L = 0
+    if k_depth is not None and k_depth.numel() > 0:
+        _check(k_depth, "k_depth", dtype, 4)
+        _check(v_depth, "v_depth", dtype, 4)
+        L = k_depth.shape[2]
+        if tuple(k_depth.shape) != (B, Hk, L, d) or tuple(v_depth.shape) != (B, Hk, L, d):
+            raise ValueError("depth K/V must be [B,Hk,L,d] = %s" % ((B, Hk, L, d),))
+    else:
+        k_depth = v_depth = None
+    _check(out, "out", dtype, 3)
+    _check(lse, "lse", torch.float32, 2)
+    if tuple(out.shape) != (B, Hq, d) or tuple(lse.shape) != (B, Hq):
+        raise ValueError("out must be [B,Hq,d] and lse [B,Hq]")
+    rc = _lib.load().moda_attn_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_depth),
+                                              _ptr(v_depth), B, T, Hq, Hk, d, L, _ptr(out), _ptr(lse),
+                                              _stream(stream))
+    if rc != MODA_OK:
+        raise MODAError("moda_attn_decode_noalloc", rc)
     return out, lse
 
 

@@ -42,10 +42,10 @@ int validate_fwd(bool bf16, const void* q, const void* k, const void* v, const v
   return MODA_OK;
 }
 
-int validate_decode(const void* q, const void* k, const void* v, const void* kd, const void* vd, int B, int T,
-                    int Hq, int Hk, int d, int Lcap, int L, const void* out, const float* lse, const void* ws,
-                    size_t ws_bytes) {
-  if (!q || !k || !v || !out || !lse || !ws) return MODA_ERR_NULL;
+// Everything moda_attn_decode checks except its workspace.
+int validate_decode_args(const void* q, const void* k, const void* v, const void* kd, const void* vd, int B, int T,
+                         int Hq, int Hk, int d, int Lcap, int L, const void* out, const float* lse) {
+  if (!q || !k || !v || !out || !lse) return MODA_ERR_NULL;
   if (L > 0 && (!kd || !vd)) return MODA_ERR_NULL;
   if (B <= 0 || T <= 0 || Hq <= 0 || Hk <= 0 || d <= 0 || L < 0 || Lcap < L) return MODA_ERR_SHAPE;
   if (Hq % Hk != 0) return MODA_ERR_SHAPE;
@@ -57,10 +57,19 @@ int validate_decode(const void* q, const void* k, const void* v, const void* kd,
     return MODA_ERR_UNSUPPORTED;
   if (moda::decode_grid_blocks(B, T, Hk, L) > INT_MAX || static_cast<int64_t>(B) * Hq > INT_MAX)
     return MODA_ERR_UNSUPPORTED;
-  if (ws_bytes < moda::decode_workspace_bytes(B, T, Hq, Hk, d, L)) return MODA_ERR_SHAPE;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse) || !aligned16(ws))
-    return MODA_ERR_ALIGN;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse)) return MODA_ERR_ALIGN;
   if (L > 0 && (!aligned16(kd) || !aligned16(vd))) return MODA_ERR_ALIGN;
+  return MODA_OK;
+}
+
+int validate_decode(const void* q, const void* k, const void* v, const void* kd, const void* vd, int B, int T,
+                    int Hq, int Hk, int d, int Lcap, int L, const void* out, const float* lse, const void* ws,
+                    size_t ws_bytes) {
+  if (!ws) return MODA_ERR_NULL;
+  const int rc = validate_decode_args(q, k, v, kd, vd, B, T, Hq, Hk, d, Lcap, L, out, lse);
+  if (rc != MODA_OK) return rc;
+  if (ws_bytes < moda::decode_workspace_bytes(B, T, Hq, Hk, d, L)) return MODA_ERR_SHAPE;
+  if (!aligned16(ws)) return MODA_ERR_ALIGN;
   return MODA_OK;
 }
 
@@ -202,6 +211,19 @@ int moda_kv_project(const void* x, const void* w_kv, int B, int T, int Dm, int H
   return moda::launch_kv_project(a) == hipSuccess ? MODA_OK : MODA_ERR_HIP;
 }
 
+int moda_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, const void* k_depth,
+                             const void* v_depth, int B, int T, int Hq, int Hk, int d, int L, void* out,
+                             float* lse, moda_stream_t stream) {
+  const int rc = validate_decode_args(q, k_cache, v_cache, k_depth, v_depth, B, T, Hq, Hk, d, L, L, out, lse);
+  if (rc != MODA_OK) return rc;
+  if (moda::decode_workspace_bytes(B, T, Hq, Hk, d, L) > moda::kDecodeScratchBytes) return MODA_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  if (moda::decode_scratch(&ws) != hipSuccess) return MODA_ERR_HIP;
+  moda::DecodeArgs a{q, k_cache, v_cache, L > 0 ? k_depth : nullptr, L > 0 ? v_depth : nullptr,
+                     B, T, Hq, Hk, d, L, L, out, lse, ws, stream};
+  return moda::launch_decode_bf16(a) == hipSuccess ? MODA_OK : MODA_ERR_HIP;
+}
+
 size_t moda_attn_decode_workspace(int B, int T, int Hq, int Hk, int d, int L) {
   if (B <= 0 || T <= 0 || Hq <= 0 || Hk <= 0 || d <= 0 || L < 0) return 0;
   if (Hq % Hk != 0) return 0;
@@ -243,6 +265,7 @@ const char* moda_error_string(int code) {
     case MODA_ERR_UNSUPPORTED: return "no kernel for this head dimension, group size or problem size";
     case MODA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case MODA_ERR_HIP: return "the HIP launch failed";
+    case MODA_ERR_TOO_LARGE: return "the problem needs more scratch than the allocation-free entry point holds";
     default: return "unknown error";
   }
 }

@@ -17,8 +17,16 @@
 // keys (16 KiB per K/V pair at d = 128, so five waves fit a CU's LDS) are
 // staged by direct-to-LDS loads, double buffered, and the score/PV steps are
 // the forward kernel's.
+#include <mutex>
+
 #include "moda_launch.h"
 #include "moda_tile.h"
+
+// Per-device scratch of the allocation-free decode entry point: it holds the
+// per-chunk partial results that moda_attn_decode keeps in the caller's
+// workspace.  Every GPU the library runs on holds one copy until the process
+// ends, and every call on that GPU shares it.
+static __device__ __align__(256) float scratch[moda::kDecodeScratchBytes / sizeof(float)];
 
 namespace moda {
 namespace {
@@ -290,6 +298,31 @@ int64_t decode_grid_blocks(int B, int T, int Hk, int L) {
 
 hipError_t launch_decode_bf16(const DecodeArgs& a) {
   return a.d == 64 ? launch_decode_d<64>(a) : launch_decode_d<128>(a);
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];  // device address of `scratch` on each device, once looked up
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    // The array's name is a host-side stand-in; the kernels need this
+    // device's own address of it, looked up once with the device current.
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    scratch_ptr[dev] = p;
+  }
+  *ptr = scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace moda

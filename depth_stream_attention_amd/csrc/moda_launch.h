@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/moda.h"
+
 namespace moda {
 
 struct FwdArgs {
@@ -53,6 +55,12 @@ int64_t fwd_f32_grid_blocks(int B, int T, int Hq);
 hipError_t launch_decode_bf16(const DecodeArgs& a);
 size_t decode_workspace_bytes(int B, int T, int Hq, int Hk, int d, int L);
 int64_t decode_grid_blocks(int B, int T, int Hk, int L);
+
+// Scratch of the allocation-free decode (a static device array per device):
+// its capacity, and its address on the current device, which the first call
+// on each device looks up.
+constexpr size_t kDecodeScratchBytes = MODA_DECODE_NOALLOC_SCRATCH_BYTES;
+hipError_t decode_scratch(void** ptr);
 
 hipError_t launch_bwd_bf16(const BwdArgs& a);
 size_t bwd_workspace_bytes(int B, int T, int Hq, int d, int L);

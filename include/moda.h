@@ -38,6 +38,7 @@ extern "C" {
 #define MODA_ERR_UNSUPPORTED (-3) /* a valid size this build has no kernel for */
 #define MODA_ERR_ALIGN (-4)       /* a pointer is not 16-byte aligned */
 #define MODA_ERR_HIP (-5)         /* the HIP launch reported an error */
+#define MODA_ERR_TOO_LARGE (-6)   /* larger than moda_attn_decode_noalloc's fixed scratch */
 
 typedef void* moda_stream_t; /* hipStream_t */
 
@@ -164,6 +165,32 @@ int moda_attn_decode_ring(const void* q, const void* k_cache, const void* v_cach
  * size is invalid): (d + 2) fp32 values per (batch, query head, chunk).
  */
 size_t moda_attn_decode_workspace(int B, int T, int Hq, int Hk, int d, int L);
+
+/*
+ * moda_attn_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  It allocates nothing and calls no
+ * allocating routine: the per-chunk partial results live in a fixed scratch
+ * array of MODA_DECODE_NOALLOC_SCRATCH_BYTES that the library holds in every
+ * GPU's memory it runs on, from the first call on that GPU until the process
+ * ends.  The first call on a device looks up that device's address of the
+ * array (with the device current); later calls reuse it.
+ *
+ * Same operation, arguments, layouts, kernels and results (bit for bit) as
+ * moda_attn_decode for the same inputs.  `stream` must belong to the current
+ * device.  All calls on one GPU share its scratch, so calls that overlap in
+ * time on one GPU (on different streams, or from different threads) race and
+ * must be serialised by the caller.  Every partial result is written before
+ * it is read, so nothing needs clearing between calls.
+ *
+ * Errors: as moda_attn_decode (there is no workspace to check), plus
+ * MODA_ERR_TOO_LARGE when moda_attn_decode_workspace(B, T, Hq, Hk, d, L)
+ * exceeds MODA_DECODE_NOALLOC_SCRATCH_BYTES (nothing is enqueued).
+ */
+#define MODA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int moda_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, const void* k_depth,
+                             const void* v_depth, int B, int T, int Hq, int Hk, int d, int L, void* out,
+                             float* lse, moda_stream_t stream);
 
 /*
  * MoDA backward, bf16 in / bf16 gradients, fp32 accumulation: the gradients of

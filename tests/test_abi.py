@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_error_strings(lib):
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         s = api.moda_error_string(code)
         assert s and s != "unknown error"
     assert api.moda_error_string(17) == "unknown error"
@@ -129,6 +129,29 @@ def test_decode_validation(lib):
         assert decode(lib, **kw) == api.MODA_ERR_UNSUPPORTED, kw
     for kw in (dict(q=MIS), dict(kc=MIS), dict(vc=MIS), dict(kd=MIS), dict(vd=MIS), dict(out=MIS), dict(ws=MIS)):
         assert decode(lib, **kw) == api.MODA_ERR_ALIGN, kw
+
+
+def test_decode_noalloc_validation(lib):
+    # every error comes from the host checks, before the scratch lookup or any launch
+    null = ctypes.c_void_p(0)
+
+    def dec(q=A, kc=A, vc=A, kd=A, vd=A, B=2, T=300, Hq=8, Hk=2, d=128, L=5, out=A2, lse=A2):
+        return lib.moda_attn_decode_noalloc(q, kc, vc, kd, vd, B, T, Hq, Hk, d, L, out, lse, None)
+
+    for kw in (dict(q=null), dict(kc=null), dict(vc=null), dict(out=null), dict(lse=null), dict(kd=null),
+               dict(vd=null)):
+        assert dec(**kw) == api.MODA_ERR_NULL, kw
+    for kw in (dict(B=0), dict(T=0), dict(Hq=0), dict(Hk=0), dict(d=0), dict(L=-1), dict(Hq=6, Hk=4)):
+        assert dec(**kw) == api.MODA_ERR_SHAPE, kw
+    for kw in (dict(d=96), dict(Hq=6, Hk=2), dict(Hq=128, Hk=2)):
+        assert dec(**kw) == api.MODA_ERR_UNSUPPORTED, kw
+    for kw in (dict(q=MIS), dict(kc=MIS), dict(vc=MIS), dict(kd=MIS), dict(vd=MIS), dict(out=MIS)):
+        assert dec(**kw) == api.MODA_ERR_ALIGN, kw
+    # the fixed scratch: the decode workspace of B=16 T=65536 Hq=16 Hk=4 d=128 L=48 fits, B=32 does not
+    cap = api.MODA_DECODE_NOALLOC_SCRATCH_BYTES
+    assert lib.moda_attn_decode_workspace(16, 65536, 16, 4, 128, 48) <= cap
+    assert lib.moda_attn_decode_workspace(32, 65536, 16, 4, 128, 48) > cap
+    assert dec(B=32, T=65536, Hq=16, Hk=4, L=48) == api.MODA_ERR_TOO_LARGE
 
 
 def test_ring_validation(lib):
