@@ -29,7 +29,7 @@ def load_probe():
         raise RuntimeError("libmoda_probe.so is not built (%s)" % PROBE_LIB_PATH)
     lib = ctypes.CDLL(PROBE_LIB_PATH)
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
-    lib.moda_probe_mfma_bf16.argtypes = [vp, i32, i32, vp]
+    lib.moda_probe_mfma_bf16.argtypes = [vp, i32, i32, i32, vp]
     lib.moda_probe_copy.argtypes = [vp, vp, sz, i32, vp]
     lib.moda_probe_read.argtypes = [vp, sz, i32, vp, vp]
     for fn in (lib.moda_probe_mfma_bf16, lib.moda_probe_copy, lib.moda_probe_read):

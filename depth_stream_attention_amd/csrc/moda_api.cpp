@@ -83,7 +83,7 @@ int validate_bwd(const void* q, const void* k, const void* v, const void* kd, co
   if (Hq % Hk != 0) return MODA_ERR_SHAPE;
   if (causal != 0 && causal != 1) return MODA_ERR_SHAPE;
   if (d != 64 && d != 128) return MODA_ERR_UNSUPPORTED;
-  if (!is_pow2_in(Hq / Hk, 1, 16)) return MODA_ERR_UNSUPPORTED;
+  if (!is_pow2_in(Hq / Hk, 1, 32)) return MODA_ERR_UNSUPPORTED;
   // One (batch) sequence of q or dO, and of one KV head's keys, is addressed
   // with 32-bit byte offsets; grids and expanded rows stay in int32.
   if (static_cast<int64_t>(T + 128) * Hq * d * 2 >= (int64_t{1} << 31)) return MODA_ERR_UNSUPPORTED;

@@ -16,8 +16,8 @@
 //   2. depth: per (token, KV head): the G rows of the token against its L depth
 //             slots.  Depth slots are seen by their own token only, so this
 //             produces dK_depth and dV_depth completely and the depth share of
-//             dq (fp32, in the workspace).  16x16 MFMA tiles: G <= 16 rows on
-//             one side, 16 slots on the other.
+//             dq (fp32, in the workspace).  16x16 MFMA tiles: 16 of the G
+//             rows on one side (G = 32 in two halves), 16 slots on the other.
 //   3. dq:    the forward's decomposition (128 expanded rows per workgroup, 32
 //             per wave, lane = query row) over 64-key sequence tiles:
 //             S^T = K Q^T, dP^T = V dO^T, dS^T, then dQ^T += K^T dS^T.  Adds the
@@ -217,20 +217,23 @@ struct Blk16 {
   }
 };
 
-template <int D>
+template <int D, int NH>
 __global__ __launch_bounds__(kThreads) void moda_bwd_depth_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout, const uint16_t* __restrict__ kd,
     const uint16_t* __restrict__ vd, const float* __restrict__ ws_l2, const float* __restrict__ ws_dd, int T, int Hq,
     int Hk, int L, int lgG, int64_t n_units, float scale, float scale_log2, float* __restrict__ dq_depth,
     uint16_t* __restrict__ dkd, uint16_t* __restrict__ dvd) {
+  // NH = 16-row halves of the unit's G rows (1 for G <= 16, 2 for G = 32): each
+  // half forms its own scores; the slot gradients sum both halves' products.
   using BK = Blk16<D>;
   constexpr int KC = D / 32;  // 16x16x32 contraction steps over d
   constexpr int DC = D / 16;  // 16-wide d tiles of the outputs
-  __shared__ __attribute__((aligned(16))) uint8_t smem_raw[kWaves * 3 * BK::BYTES];
+  constexpr int PER_WAVE = (2 * NH + 1) * BK::BYTES;  // Q and dO rows of every half, one Kd step
+  __shared__ __attribute__((aligned(16))) uint8_t smem_raw[kWaves * PER_WAVE];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const uint32_t qs = lds_addr((lds_u8*)smem_raw) + wave * 3 * BK::BYTES;
-  const uint32_t os = qs + BK::BYTES, ks = os + BK::BYTES;
+  const uint32_t qs = lds_addr((lds_u8*)smem_raw) + wave * PER_WAVE;  // half h: qs + h * BYTES
+  const uint32_t os = qs + NH * BK::BYTES, ks = os + NH * BK::BYTES;
   const int G = 1 << lgG;
   const int r16 = lane & 15, grp = lane >> 4;
 
@@ -255,33 +258,40 @@ __global__ __launch_bounds__(kThreads) void moda_bwd_depth_kernel(
     const int64_t b = bt / T;
     const int64_t row0 = (bt * Hq + static_cast<int64_t>(hk) * G) * D;  // element offset of the unit's first row
 
-    bf16x8 qf[KC], of[KC];
+    bf16x8 qf[NH][KC], of[NH][KC];
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
-      if (r16 < G) {
-        a = *reinterpret_cast<const u32x4*>(q + row0 + r16 * D + (4 * kc + grp) * 8);
-        c = *reinterpret_cast<const u32x4*>(dout + row0 + r16 * D + (4 * kc + grp) * 8);
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
+        if (16 * h + r16 < G) {
+          a = *reinterpret_cast<const u32x4*>(q + row0 + (16 * h + r16) * D + (4 * kc + grp) * 8);
+          c = *reinterpret_cast<const u32x4*>(dout + row0 + (16 * h + r16) * D + (4 * kc + grp) * 8);
+        }
+        qf[h][kc] = __builtin_bit_cast(bf16x8, a);
+        of[h][kc] = __builtin_bit_cast(bf16x8, c);
+        *lds_at<lds_bf16x8_t>(qs + h * BK::BYTES + nrm[kc]) = qf[h][kc];
+        *lds_at<lds_bf16x8_t>(os + h * BK::BYTES + nrm[kc]) = of[h][kc];
       }
-      qf[kc] = __builtin_bit_cast(bf16x8, a);
-      of[kc] = __builtin_bit_cast(bf16x8, c);
-      *lds_at<lds_bf16x8_t>(qs + nrm[kc]) = qf[kc];
-      *lds_at<lds_bf16x8_t>(os + nrm[kc]) = of[kc];
-    }
     const int64_t e0 = ((b * Hk + hk) * T + t) * G;  // expanded index of the unit's row 0
-    const float l2T = r16 < G ? ws_l2[e0 + r16] : INFINITY;
-    const float ddT = r16 < G ? ws_dd[e0 + r16] : 0.0f;
-    float l2S[4], ddS[4];
+    float l2T[NH], ddT[NH], l2S[NH][4], ddS[NH][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rr = 4 * grp + i;
-      l2S[i] = rr < G ? ws_l2[e0 + rr] : INFINITY;
-      ddS[i] = rr < G ? ws_dd[e0 + rr] : 0.0f;
+    for (int h = 0; h < NH; ++h) {
+      l2T[h] = 16 * h + r16 < G ? ws_l2[e0 + 16 * h + r16] : INFINITY;
+      ddT[h] = 16 * h + r16 < G ? ws_dd[e0 + 16 * h + r16] : 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rr = 16 * h + 4 * grp + i;
+        l2S[h][i] = rr < G ? ws_l2[e0 + rr] : INFINITY;
+        ddS[h][i] = rr < G ? ws_dd[e0 + rr] : 0.0f;
+      }
     }
 
-    f32x4 dqa[DC];
+    f32x4 dqa[NH][DC];
 #pragma unroll
-    for (int dc = 0; dc < DC; ++dc) dqa[dc] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) dqa[h][dc] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     const int64_t slab = u * static_cast<int64_t>(L) * D;  // packed [B][T][Hk][L][d]: slab index = u
 
     // Depth K/V rows of one 16-slot step (zero past slot L), the next step's
@@ -313,34 +323,41 @@ __global__ __launch_bounds__(kThreads) void moda_bwd_depth_kernel(
       if (c0 + 16 < L) load_step(c0 + 16, kn, vn);
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) *lds_at<lds_bf16x8_t>(ks + nrm[kc]) = kf[kc];
-      f32x4 S = {}, dP = {}, ST = {}, dPT = {};
+      s16x4 P4[NH], DS4[NH], DST4[NH];
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        S = mfma16x32(qf[kc], kf[kc], S);     // [row 4*grp+i][slot r16]
-        dP = mfma16x32(of[kc], vf[kc], dP);
-        ST = mfma16x32(kf[kc], qf[kc], ST);   // [slot 4*grp+i][row r16]
-        dPT = mfma16x32(vf[kc], of[kc], dPT);
-      }
-      float p[4], ds[4], dst[4];
+      for (int h = 0; h < NH; ++h) {
+        f32x4 S = {}, dP = {}, ST = {}, dPT = {};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[i] = valid ? fast_exp2(fmaf(S[i], scale_log2, -l2S[i])) : 0.0f;
-        ds[i] = p[i] * (dP[i] - ddS[i]);
-        const bool vt = c0 + 4 * grp + i < L;
-        const float pt = vt ? fast_exp2(fmaf(ST[i], scale_log2, -l2T)) : 0.0f;
-        dst[i] = pt * (dPT[i] - ddT);
+        for (int kc = 0; kc < KC; ++kc) {
+          S = mfma16x32(qf[h][kc], kf[kc], S);     // [row 16h+4*grp+i][slot r16]
+          dP = mfma16x32(of[h][kc], vf[kc], dP);
+          ST = mfma16x32(kf[kc], qf[h][kc], ST);   // [slot 4*grp+i][row 16h+r16]
+          dPT = mfma16x32(vf[kc], of[h][kc], dPT);
+        }
+        float p[4], ds[4], dst[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[i] = valid ? fast_exp2(fmaf(S[i], scale_log2, -l2S[h][i])) : 0.0f;
+          ds[i] = p[i] * (dP[i] - ddS[h][i]);
+          const bool vt = c0 + 4 * grp + i < L;
+          const float pt = vt ? fast_exp2(fmaf(ST[i], scale_log2, -l2T[h])) : 0.0f;
+          dst[i] = pt * (dPT[i] - ddT[h]);
+        }
+        P4[h] = pack4(p[0], p[1], p[2], p[3]);
+        DS4[h] = pack4(ds[0], ds[1], ds[2], ds[3]);
+        DST4[h] = pack4(dst[0], dst[1], dst[2], dst[3]);
       }
-      const s16x4 P4 = pack4(p[0], p[1], p[2], p[3]);
-      const s16x4 DS4 = pack4(ds[0], ds[1], ds[2], ds[3]);
-      const s16x4 DST4 = pack4(dst[0], dst[1], dst[2], dst[3]);
       uint16_t* dk_row = dkd + slab + static_cast<int64_t>(slot) * D + 4 * grp;
       uint16_t* dv_row = dvd + slab + static_cast<int64_t>(slot) * D + 4 * grp;
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) {
-        const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-        const f32x4 gv = mfma16x16(read_tr(os + trd[dc]), P4, zero);   // [d 16dc+4grp+i][slot r16]
-        const f32x4 gk = mfma16x16(read_tr(qs + trd[dc]), DS4, zero);
-        dqa[dc] = mfma16x16(read_tr(ks + trd[dc]), DST4, dqa[dc]);     // [d 16dc+4grp+i][row r16]
+        f32x4 gv = {0.0f, 0.0f, 0.0f, 0.0f}, gk = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+          gv = mfma16x16(read_tr(os + h * BK::BYTES + trd[dc]), P4[h], gv);   // [d 16dc+4grp+i][slot r16]
+          gk = mfma16x16(read_tr(qs + h * BK::BYTES + trd[dc]), DS4[h], gk);
+          dqa[h][dc] = mfma16x16(read_tr(ks + trd[dc]), DST4[h], dqa[h][dc]);  // [d 16dc+4grp+i][row 16h+r16]
+        }
         if (valid) {
           u32x2 wv = {pack_bf16x2(gv[0], gv[1]), pack_bf16x2(gv[2], gv[3])};
           u32x2 wk = {pack_bf16x2(gk[0] * scale, gk[1] * scale), pack_bf16x2(gk[2] * scale, gk[3] * scale)};
@@ -349,11 +366,13 @@ __global__ __launch_bounds__(kThreads) void moda_bwd_depth_kernel(
         }
       }
     }
-    if (r16 < G) {
-      float* dqr = dq_depth + row0 + r16 * D + 4 * grp;
 #pragma unroll
-      for (int dc = 0; dc < DC; ++dc) *reinterpret_cast<f32x4*>(dqr + 16 * dc) = dqa[dc] * scale;
-    }
+    for (int h = 0; h < NH; ++h)
+      if (16 * h + r16 < G) {
+        float* dqr = dq_depth + row0 + (16 * h + r16) * D + 4 * grp;
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) *reinterpret_cast<f32x4*>(dqr + 16 * dc) = dqa[h][dc] * scale;
+      }
   }
 }
 
@@ -981,10 +1000,16 @@ hipError_t launch_bwd_d(const BwdArgs& a) {
   if (a.L > 0) {
     const int64_t units = static_cast<int64_t>(a.B) * a.T * a.Hk;
     const int64_t blocks = std::min<int64_t>((units + kWaves - 1) / kWaves, kDepthBlocks);
-    hipLaunchKernelGGL((moda_bwd_depth_kernel<D>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st, q, dout,
-                       static_cast<const uint16_t*>(a.kd), static_cast<const uint16_t*>(a.vd), l2, dd, a.T, a.Hq, a.Hk,
-                       a.L, lgG, units, scale, scale_log2, dqd, static_cast<uint16_t*>(a.dkd),
-                       static_cast<uint16_t*>(a.dvd));
+    if (G <= 16)
+      hipLaunchKernelGGL((moda_bwd_depth_kernel<D, 1>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st, q,
+                         dout, static_cast<const uint16_t*>(a.kd), static_cast<const uint16_t*>(a.vd), l2, dd, a.T,
+                         a.Hq, a.Hk, a.L, lgG, units, scale, scale_log2, dqd, static_cast<uint16_t*>(a.dkd),
+                         static_cast<uint16_t*>(a.dvd));
+    else
+      hipLaunchKernelGGL((moda_bwd_depth_kernel<D, 2>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st, q,
+                         dout, static_cast<const uint16_t*>(a.kd), static_cast<const uint16_t*>(a.vd), l2, dd, a.T,
+                         a.Hq, a.Hk, a.L, lgG, units, scale, scale_log2, dqd, static_cast<uint16_t*>(a.dkd),
+                         static_cast<uint16_t*>(a.dvd));
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

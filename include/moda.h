@@ -229,7 +229,7 @@ int moda_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_c
  * Errors: MODA_ERR_NULL (a required pointer NULL; depth inputs or gradients
  * NULL with L > 0); MODA_ERR_SHAPE (a size <= 0, L < 0, Hq % Hk != 0,
  * causal not 0/1, or workspace_bytes below moda_attn_bwd_workspace);
- * MODA_ERR_UNSUPPORTED (d not 64 or 128; G not in {1,2,4,8,16}; (T + 128) *
+ * MODA_ERR_UNSUPPORTED (d not 64 or 128; G not in {1,2,4,8,16,32}; (T + 128) *
  * Hq * d * 2 bytes or a grid beyond 2^31); MODA_ERR_ALIGN; MODA_ERR_HIP.
  */
 int moda_attn_bwd(const void* q, const void* k_seq, const void* v_seq, const void* k_depth, const void* v_depth,

@@ -199,8 +199,8 @@ def test_bwd_validation(lib):
                dict(causal=2)):
         assert bwd(lib, **kw) == api.MODA_ERR_SHAPE, kw
     assert bwd(lib, ws_bytes=lib.moda_attn_bwd_workspace(2, 300, 8, 2, 128, 5) - 4) == api.MODA_ERR_SHAPE
-    # G = 32 has a forward but no backward; sizes beyond the 32-bit offsets are refused
-    for kw in (dict(d=96), dict(Hq=6, Hk=2), dict(Hq=64, Hk=2), dict(T=1 << 20, Hq=16, Hk=2)):
+    # G = 64 has no kernel; sizes beyond the 32-bit offsets are refused
+    for kw in (dict(d=96), dict(Hq=6, Hk=2), dict(Hq=128, Hk=2), dict(T=1 << 20, Hq=16, Hk=2)):
         assert bwd(lib, **kw) == api.MODA_ERR_UNSUPPORTED, kw
     for name in ("q", "k", "v", "kd", "vd", "out", "lse", "do", "dq", "dk", "dv", "dkd", "dvd", "ws"):
         assert bwd(lib, **{name: MIS}) == api.MODA_ERR_ALIGN, name
@@ -233,10 +233,11 @@ def test_probe_library_exports_and_validates():
     for n in names:
         assert hasattr(probe, n), "libmoda_probe.so does not export %s" % n
     null = ctypes.c_void_p(0)
-    assert probe.moda_probe_mfma_bf16(null, 4, 4, None) == api.MODA_ERR_NULL
-    assert probe.moda_probe_mfma_bf16(A, 0, 4, None) == api.MODA_ERR_SHAPE
-    assert probe.moda_probe_mfma_bf16(A, 4, 0, None) == api.MODA_ERR_SHAPE
-    assert probe.moda_probe_mfma_bf16(MIS, 4, 4, None) == api.MODA_ERR_ALIGN
+    assert probe.moda_probe_mfma_bf16(null, 4, 4, 1, None) == api.MODA_ERR_NULL
+    assert probe.moda_probe_mfma_bf16(A, 0, 4, 1, None) == api.MODA_ERR_SHAPE
+    assert probe.moda_probe_mfma_bf16(A, 4, 0, 1, None) == api.MODA_ERR_SHAPE
+    assert probe.moda_probe_mfma_bf16(A, 4, 4, 2, None) == api.MODA_ERR_SHAPE
+    assert probe.moda_probe_mfma_bf16(MIS, 4, 4, 1, None) == api.MODA_ERR_ALIGN
     assert probe.moda_probe_copy(null, A2, 64, 4, None) == api.MODA_ERR_NULL
     assert probe.moda_probe_copy(A, A2, 63, 4, None) == api.MODA_ERR_SHAPE
     assert probe.moda_probe_copy(A, A2, 0, 4, None) == api.MODA_ERR_SHAPE

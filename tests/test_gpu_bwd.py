@@ -78,10 +78,17 @@ def test_bwd_sequence_lengths(T):
     bwd_case(S(2, T, 8, 2, 128, 5), 800 + T)
 
 
-@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16, 32])
 @pytest.mark.parametrize("d", [64, 128])
 def test_bwd_group_sizes(G, d):
     bwd_case(S(1, 200, 2 * G, 2, d, 6), 850 + 10 * G + d)
+
+
+@pytest.mark.parametrize("L", [1, 16, 40])
+def test_bwd_32_heads_per_kv_head(L):
+    # G = 32: a token's rows are two 16-row halves in the depth-gradient kernel, whose slot
+    # gradients sum both halves; one, one whole and two and a half 16-slot steps
+    bwd_case(S(2, 97, 64, 2, 128, L), 870 + L)
 
 
 @pytest.mark.parametrize("L", [0, 1, 15, 16, 17, 48])
