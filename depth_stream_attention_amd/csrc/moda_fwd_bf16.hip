@@ -421,6 +421,8 @@ hipError_t launch_d(const FwdArgs& a) {
 
 }  // namespace
 
+int fwd_bf16_rows_per_block() { return kBM; }
+
 int64_t fwd_bf16_grid_blocks(int B, int T, int Hq, int Hk) {
   const int64_t TG = static_cast<int64_t>(T) * (Hq / Hk);
   return (TG + kBM - 1) / kBM * B * Hk;
