@@ -51,9 +51,9 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
-    on the current kernel source; otherwise None."""
+def traffic_record():
+    """The committed rocprofv3 counter record of the forward (HBM bytes per launch of the
+    L=48 and L=0 kernels), if it was taken on the current kernel source; otherwise None."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
@@ -61,7 +61,7 @@ def measured_traffic():
         return None
     if rec.get("kernel_source_hash") != kernel_source_hash():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec
 
 
 def cpu_baseline(shape, host, budget_s):
@@ -271,11 +271,12 @@ def summarize(trace_dir, fetch_dir, write_dir, command, sq_dir=None):
         "  commands: " + command[1], "            " + command[2],
         "  calibration on moda_pack_depth (reads and writes %d bytes): FETCH_SIZE x %.4f, WRITE_SIZE x %.4f"
         % (pack_bytes, f_scale, w_scale), ""]
-    traffic = {}
+    traffic, reads = {}, {}
     for lab in ("moda_fwd_bf16 L=48", "moda_fwd_bf16 L=0", "moda_pack_depth"):
         rd = counters["FETCH_SIZE"].get(lab, 0.0) * f_scale
         wr = counters["WRITE_SIZE"].get(lab, 0.0) * w_scale
         traffic[lab] = rd + wr
+        reads[lab] = rd
         lines.append("  %-22s read %.4g B  write %.4g B  total %.4g B" % (lab, rd, wr, rd + wr))
     alg = acc.algorithmic_bytes(shape)
     lines.append("  algorithmic bytes of the L=48 forward: %.4g B (traffic / algorithmic = %.3f)"
@@ -294,6 +295,8 @@ def summarize(trace_dir, fetch_dir, write_dir, command, sq_dir=None):
     with open(TRAFFIC_FILE, "w") as f:
         json.dump({"kernel": "moda_fwd_bf16 L=48", "kernel_source_hash": kernel_source_hash(),
                    "hbm_bytes_per_launch": traffic["moda_fwd_bf16 L=48"],
+                   "read_bytes_per_launch": reads["moda_fwd_bf16 L=48"],
+                   "l0_read_bytes_per_launch": reads["moda_fwd_bf16 L=0"],
                    "fetch_scale": f_scale, "write_scale": w_scale}, f, indent=1)
     print("\n".join(lines))
 
@@ -667,7 +670,8 @@ def main():
     Fseq = acc.flops_seq(shape.B, shape.T, shape.Hq, shape.d)
     tflops = F / (fwd_ms * 1e-3) / 1e12
     tflops0 = F0 / (fwd0_ms * 1e-3) / 1e12
-    traffic = measured_traffic()
+    trec = traffic_record()
+    traffic = trec.get("hbm_bytes_per_launch") if trec else None
     rec = {
         "metric": "MoDA fwd TFLOP/s + time ratio vs L=0 causal attn, bf16, T=64K, 1 MI355X",
         "value": round(tflops, 2),
@@ -696,6 +700,9 @@ def main():
         "l0_tflops": round(tflops0, 2),
         "seq_mfma_util": round(Fseq / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "depth_marginal_gbs": round(acc.depth_bytes(shape) / max(1e-9, (fwd_ms - fwd0_ms) * 1e-3) / 1e9, 1),
+        "depth_hbm_gbs_counters": (round((trec["read_bytes_per_launch"] - trec["l0_read_bytes_per_launch"])
+                                         / (fwd_ms * 1e-3) / 1e9, 1)
+                                   if trec and "l0_read_bytes_per_launch" in trec else None),
         "pack_gbs": round(2 * acc.depth_bytes(shape) / (pack_ms * 1e-3) / 1e9, 1),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
