@@ -405,14 +405,13 @@ __device__ __forceinline__ void dma_kv(const uint16_t* kb, const uint16_t* vb, u
   constexpr int NX = kNX<D>;
   const int64_t first = static_cast<int64_t>(idx) * kBN * Hk * D;
   const uint32_t range = seq_range - static_cast<uint32_t>(idx * kBN) * key_bytes;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb + first, range);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb + first, range);
+  const u32x4 rk = raw_rsrc(kb + first, range);
+  const u32x4 rv = raw_rsrc(vb + first, range);
 #pragma unroll
   for (int x = 0; x < NX; ++x) {
-    lds_u8* dst = buf + (wave * NX + x) * 1024;
-    const uint32_t ok = o.k[x], ov = o.v[x];  // (builtin operands must not be references)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)dst, 16, ok, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(dst + TL::BYTES), 16, ov, 0, 0, 0);
+    const uint32_t dst = lds_addr(buf + (wave * NX + x) * 1024);
+    dma16(rk, dst, o.k[x]);
+    dma16(rv, dst + TL::BYTES, o.v[x]);
   }
 }
 

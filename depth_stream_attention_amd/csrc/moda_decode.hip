@@ -57,7 +57,7 @@ int decode_chunks(int B, int T, int Hk, int L) { return decode_seq_chunks(B, T, 
 // logical chunk pc ^ swz(pr).  Rows past the chunk's end fall outside the
 // descriptors' ranges and read as zero.
 template <int D>
-__device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, uint32_t stride,
+__device__ __forceinline__ void dma_rows(const u32x4& rk, const u32x4& rv, uint32_t stride,
                                          int first, lds_u8* buf, int lane) {
   using TL = Tile<D>;
   lane = opaque(lane);  // recompute the per-lane offsets here rather than hold 2 * 64 / RPI registers
@@ -68,9 +68,9 @@ __device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t rk, __amdgpu_buf
     const uint32_t row = static_cast<uint32_t>(first + pr) * stride;
     const uint32_t ok = row + ((pc ^ TL::swz_k(pr)) * 16);
     const uint32_t ov = row + ((pc ^ TL::swz_v(pr)) * 16);
-    lds_u8* dk = buf + x * 1024;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)dk, 16, ok, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(dk + kTileBytes<D>), 16, ov, 0, 0, 0);
+    const uint32_t dk = lds_addr(buf + x * 1024);
+    dma16(rk, dk, ok);
+    dma16(rv, dk + kTileBytes<D>, ov);
   }
 }
 
@@ -115,8 +115,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 4))) void
     nkeys = min(chunk, T - key0);
   }
   const uint32_t range = static_cast<uint32_t>(nkeys - 1) * stride + D * 2;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase, range);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase, range);
+  const u32x4 rk = raw_rsrc(kbase, range);
+  const u32x4 rv = raw_rsrc(vbase, range);
   const int ntile = (nkeys + kRows - 1) / kRows;
 
   // Q^T fragments: row r is head hk*G + r (zero for r >= G).

@@ -66,7 +66,7 @@ constexpr int kNX = Tile<D>::CH / kWaves;
 //   depth   : base &x[b][t_b][hk][0][0] with t_b the workgroup's first token;
 //             token t_b + u, slot i at byte (u*Hk*L + i) * d*2.
 struct Geo {
-  __amdgpu_buffer_rsrc_t kd, vd;
+  u32x4 kd, vd;  // raw buffer descriptors (see raw_rsrc)
   int L;
   uint32_t key_bytes;   // Hk*d*2: stride between consecutive keys of one KV head
   uint32_t tok_bytes;   // Hk*Lcap*d*2: stride between consecutive tokens' depth slabs
@@ -95,9 +95,9 @@ __device__ __forceinline__ void dma_depth(const Geo& g, int idx, int nchunk, lds
     const bool valid = slot < g.L;
     const uint32_t ok = valid ? row_off + ((pc ^ TL::swz_k(pr)) * 16) : kOutOfRange;  // selects, not branches
     const uint32_t ov = valid ? row_off + ((pc ^ TL::swz_v(pr)) * 16) : kOutOfRange;
-    lds_u8* dk = buf + (wave * kNX<D> + x) * 1024;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(g.kd, (lds_void_t*)dk, 16, ok, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(g.vd, (lds_void_t*)(dk + TL::BYTES), 16, ov, 0, 0, 0);
+    const uint32_t dk = lds_addr(buf + (wave * kNX<D> + x) * 1024);
+    dma16(g.kd, dk, ok);
+    dma16(g.vd, dk + TL::BYTES, ov);
   }
 }
 
@@ -149,14 +149,13 @@ __device__ __forceinline__ void dma_seq(const uint16_t* kb, const uint16_t* vb, 
   using TL = Tile<D>;
   const int64_t first = static_cast<int64_t>(idx) * kBN * Hk * D;  // elements
   const uint32_t range = seq_range - static_cast<uint32_t>(idx * kBN) * key_bytes;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb + first, range);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb + first, range);
+  const u32x4 rk = raw_rsrc(kb + first, range);
+  const u32x4 rv = raw_rsrc(vb + first, range);
 #pragma unroll
   for (int x = 0; x < kNX<D>; ++x) {
-    lds_u8* dk = buf + (wave * kNX<D> + x) * 1024;
-    const uint32_t ok = lo.dk[x], ov = lo.dv[x];
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)dk, 16, ok, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(dk + TL::BYTES), 16, ov, 0, 0, 0);
+    const uint32_t dk = lds_addr(buf + (wave * kNX<D> + x) * 1024);
+    dma16(rk, dk, lo.dk[x]);
+    dma16(rv, dk + TL::BYTES, lo.dv[x]);
   }
 }
 
@@ -242,8 +241,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int64_t slab0 = ((static_cast<int64_t>(b) * T + tb) * Hk + hk) * static_cast<int64_t>(Lcap) * D;
     const int64_t range = ((static_cast<int64_t>(T - 1 - tb) * Hk + 1) * Lcap) * D * 2;
     const uint32_t dr = static_cast<uint32_t>(range < 0x7fffffff ? range : 0x7fffffff);
-    g.kd = make_rsrc(kd + slab0, dr);
-    g.vd = make_rsrc(vd + slab0, dr);
+    g.kd = raw_rsrc(kd + slab0, dr);
+    g.vd = raw_rsrc(vd + slab0, dr);
   }
   LaneOffs<D> lo;
   init_offsets<D>(lo, lane, wave, g.key_bytes);

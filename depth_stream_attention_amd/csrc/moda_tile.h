@@ -52,6 +52,26 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint16_t* base
                                            static_cast<int>(bytes), kBufFlags);
 }
 
+// A raw buffer descriptor as four scalar dwords (the same fields as
+// make_rsrc: base address, stride 0, `bytes` records of one byte).
+__device__ __forceinline__ u32x4 raw_rsrc(const uint16_t* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4{static_cast<uint32_t>(a), static_cast<uint32_t>(a >> 32) & 0xffffu, bytes,
+               static_cast<uint32_t>(kBufFlags)};
+}
+
+// One direct-to-LDS load of 16 bytes per lane (the wave fills 1 KiB at LDS
+// byte address `lds`), issued as inline asm so that the compiler does not know
+// a load into LDS is in flight.  Knowing it, the compiler makes every
+// transposed LDS read (a builtin) wait for all such loads first -- in a double
+// buffered pipeline that is the next tile's load, in the middle of the current
+// tile.  Visibility is the pipeline's own explicit vmcnt wait and barrier.
+// The s_nop covers the M0 write -> LDS-DMA hazard (the compiler sets M0 just
+// before the statement).
+__device__ __forceinline__ void dma16(const u32x4& rsrc, uint32_t lds, uint32_t voff) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
+}
+
 // Running softmax state of one query row held by a lane pair (l, l ^ 32).
 template <int D>
 struct RowState {
