@@ -36,7 +36,7 @@ int validate_fwd(bool bf16, const void* q, const void* k, const void* v, const v
   // workgroup's depth slabs (at most one token per expanded row of the
   // workgroup) with 32-bit byte offsets.
   if (bf16 && (static_cast<int64_t>(T + 64) * Hk * d * 2 >= (int64_t{1} << 31) ||
-               static_cast<int64_t>(moda::fwd_bf16_rows_per_block() + 1) * Hk * Lcap * d * 2 >=
+               static_cast<int64_t>(moda::fwd_bf16_rows_per_block(T) + 1) * Hk * Lcap * d * 2 >=
                    (int64_t{1} << 31)))
     return MODA_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse)) return MODA_ERR_ALIGN;

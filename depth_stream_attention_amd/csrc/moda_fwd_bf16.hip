@@ -48,15 +48,25 @@
 namespace moda {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
 constexpr int kRowsPerWave = 32;
-constexpr int kBM = kWaves * kRowsPerWave;  // expanded rows per workgroup
-constexpr int kDepthRowsPerWave = kBN / kWaves;
+// W waves per workgroup (4, or 8 for long sequences): W * 32 expanded rows.
+template <int W>
+constexpr int kBM = W * kRowsPerWave;
+// Sequences at least this long run 8-wave workgroups (one per CU), which stage
+// each K/V tile once for 256 rows; shorter ones run two 4-wave workgroups per CU.
+constexpr int kLongT = 32768;
+__host__ __device__ constexpr int waves_for(int T) { return T >= kLongT ? 8 : 4; }
+constexpr int kDepthRowsPerWave = 16;                     // slots of one token per wave in a depth tile
 
 // Direct-to-LDS load instructions per wave per K (or V) tile.
+template <int D, int W>
+constexpr int kNX = Tile<D>::CH / W;  // sequence-tile loads per wave per matrix
 template <int D>
-constexpr int kNX = Tile<D>::CH / kWaves;
+constexpr int kNXD = kDepthRowsPerWave * Tile<D>::ROW_BYTES / 1024;  // depth-tile loads per wave per matrix
+// An LDS buffer holds K in its first kHalf bytes and V in the next: a depth
+// tile has W * 16 rows, a sequence tile kBN rows (the first Tile::BYTES of each).
+template <int D, int W>
+constexpr int kHalf = (W * kDepthRowsPerWave > kBN ? W * kDepthRowsPerWave : kBN) * Tile<D>::ROW_BYTES;
 
 // Per-workgroup staging geometry.  All global tile reads are raw buffer loads
 // against four descriptors whose ranges end exactly at the last valid row, so
@@ -74,20 +84,20 @@ struct Geo {
 };
 
 // Direct-to-LDS loads of depth tile `idx` into `buf` (K at buf, V at
-// buf + BYTES).  For every wave w the tile holds token w*tok_wave + dtok of
+// buf + kHalf).  For every wave w the tile holds token w*tok_wave + dtok of
 // the workgroup, slots [16*dch, 16*dch + 16), at tile rows [16w, 16w + 16).
-// Instruction x of wave w fills tile rows pr = (w*NX + x)*RPI + lane/CH,
+// Instruction x of wave w fills tile rows pr = (w*NXD + x)*RPI + lane/CH,
 // physical chunk pc = lane % CH, with logical chunk pc ^ swz(pr).  Padding
 // slots (>= L) get an offset past the descriptor range and read as zero.
-template <int D>
+template <int D, int W>
 __device__ __forceinline__ void dma_depth(const Geo& g, int idx, int nchunk, lds_u8* buf, int wave, int lane) {
   using TL = Tile<D>;
   lane = opaque(lane);  // per-lane offsets below are recomputed per tile, not held across the loop
   const int dtok = idx / nchunk;
   const int dch = idx - dtok * nchunk;
 #pragma unroll
-  for (int x = 0; x < kNX<D>; ++x) {
-    const int pr = (wave * kNX<D> + x) * TL::RPI + lane / TL::CH;
+  for (int x = 0; x < kNXD<D>; ++x) {
+    const int pr = (wave * kNXD<D> + x) * TL::RPI + lane / TL::CH;
     const int pc = lane % TL::CH;
     const int slot = dch * kDepthRowsPerWave + (pr % kDepthRowsPerWave);
     const uint32_t row_off = static_cast<uint32_t>(wave * g.tok_wave + dtok) * g.tok_bytes +
@@ -95,9 +105,9 @@ __device__ __forceinline__ void dma_depth(const Geo& g, int idx, int nchunk, lds
     const bool valid = slot < g.L;
     const uint32_t ok = valid ? row_off + ((pc ^ TL::swz_k(pr)) * 16) : kOutOfRange;  // selects, not branches
     const uint32_t ov = valid ? row_off + ((pc ^ TL::swz_v(pr)) * 16) : kOutOfRange;
-    const uint32_t dk = lds_addr(buf + (wave * kNX<D> + x) * 1024);
+    const uint32_t dk = lds_addr(buf + (wave * kNXD<D> + x) * 1024);
     dma16(g.kd, dk, ok);
-    dma16(g.vd, dk + TL::BYTES, ov);
+    dma16(g.vd, dk + kHalf<D, W>, ov);
   }
 }
 
@@ -106,15 +116,15 @@ __device__ __forceinline__ void dma_depth(const Geo& g, int idx, int nchunk, lds
 // (the 32-key block, 16-key group or second half of a transposed read), so a
 // tile costs one add per distinct register instead of a full address
 // computation per read, and the sequence-tile loads need no address work.
-template <int D>
+template <int D, int W>
 struct LaneOffs {
   uint32_t kr[D / 16];                        // K read of slice sl, tile rows 0..31 (rows 32..63: + 32 rows)
   uint32_t vr[D / 32];                        // V transposed read of d tile dt, keys 0..15 (others: + rows)
-  uint32_t dk[kNX<D>], dv[kNX<D>];  // sequence-tile loads, relative to the tile's first key
+  uint32_t dk[kNX<D, W>], dv[kNX<D, W>];  // sequence-tile loads, relative to the tile's first key
 };
 
-template <int D>
-__device__ __forceinline__ void init_offsets(LaneOffs<D>& lo, int lane, int wave, uint32_t key_bytes) {
+template <int D, int W>
+__device__ __forceinline__ void init_offsets(LaneOffs<D, W>& lo, int lane, int wave, uint32_t key_bytes) {
   using TL = Tile<D>;
   const int r = lane & 31, half = lane >> 5;
 #pragma unroll
@@ -130,8 +140,8 @@ __device__ __forceinline__ void init_offsets(LaneOffs<D>& lo, int lane, int wave
   // Load instruction x of wave w fills tile rows pr = (w*NX + x)*RPI + lane/CH,
   // physical chunk pc = lane % CH, with logical chunk pc ^ swz(pr).
 #pragma unroll
-  for (int x = 0; x < kNX<D>; ++x) {
-    const int pr = (wave * kNX<D> + x) * TL::RPI + lane / TL::CH;
+  for (int x = 0; x < kNX<D, W>; ++x) {
+    const int pr = (wave * kNX<D, W> + x) * TL::RPI + lane / TL::CH;
     const int pc = lane % TL::CH;
     lo.dk[x] = static_cast<uint32_t>(pr) * key_bytes + ((pc ^ TL::swz_k(pr)) * 16);
     lo.dv[x] = static_cast<uint32_t>(pr) * key_bytes + ((pc ^ TL::swz_v(pr)) * 16);
@@ -139,23 +149,23 @@ __device__ __forceinline__ void init_offsets(LaneOffs<D>& lo, int lane, int wave
 }
 
 // Direct-to-LDS loads of sequence tile `idx` into `buf` (K at buf, V at
-// buf + BYTES), through descriptors rebased to the tile's first key (scalar
+// buf + kHalf), through descriptors rebased to the tile's first key (scalar
 // work), so the per-lane offsets are loop invariant.  Keys past the sequence
 // end fall outside the range and read as zero.
-template <int D>
+template <int D, int W>
 __device__ __forceinline__ void dma_seq(const uint16_t* kb, const uint16_t* vb, uint32_t seq_range,
                                         uint32_t key_bytes, int Hk, int idx, lds_u8* buf, int wave,
-                                        const LaneOffs<D>& lo) {
+                                        const LaneOffs<D, W>& lo) {
   using TL = Tile<D>;
   const int64_t first = static_cast<int64_t>(idx) * kBN * Hk * D;  // elements
   const uint32_t range = seq_range - static_cast<uint32_t>(idx * kBN) * key_bytes;
   const u32x4 rk = raw_rsrc(kb + first, range);
   const u32x4 rv = raw_rsrc(vb + first, range);
 #pragma unroll
-  for (int x = 0; x < kNX<D>; ++x) {
-    const uint32_t dk = lds_addr(buf + (wave * kNX<D> + x) * 1024);
+  for (int x = 0; x < kNX<D, W>; ++x) {
+    const uint32_t dk = lds_addr(buf + (wave * kNX<D, W> + x) * 1024);
     dma16(rk, dk, lo.dk[x]);
-    dma16(rv, dk + TL::BYTES, lo.dv[x]);
+    dma16(rv, dk + kHalf<D, W>, lo.dv[x]);
   }
 }
 
@@ -166,14 +176,14 @@ struct TileAddr {
   uint32_t v[D / 32];
 };
 
-template <int D>
-__device__ __forceinline__ TileAddr<D> tile_addr(const lds_u8* buf, const LaneOffs<D>& lo) {
+template <int D, int W>
+__device__ __forceinline__ TileAddr<D> tile_addr(const lds_u8* buf, const LaneOffs<D, W>& lo) {
   TileAddr<D> a;
   const uint32_t base = lds_addr(buf);
 #pragma unroll
   for (int sl = 0; sl < D / 16; ++sl) a.k[sl] = base + lo.kr[sl];
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) a.v[dt] = base + Tile<D>::BYTES + lo.vr[dt];
+  for (int dt = 0; dt < D / 32; ++dt) a.v[dt] = base + kHalf<D, W> + lo.vr[dt];
   return a;
 }
 
@@ -207,13 +217,15 @@ __device__ __forceinline__ void seq_tile(RowState<D>& st, const bf16x8 (&qf)[D /
   for (int g = 0; g < 4; ++g) pv_group<D>(st, pb[g], ta.v, 16 * g * TL::ROW_BYTES);
 }
 
-template <int D, bool DEPTH, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void moda_fwd_bf16_kernel(
+template <int D, bool DEPTH, bool CAUSAL, int W>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void moda_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ kd, const uint16_t* __restrict__ vd, int B, int T, int Hq, int Hk, int L,
     int Lcap, int lgG, int nrb, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
   using TL = Tile<D>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[4 * TL::BYTES];
+  constexpr int kBMW = kBM<W>;
+  constexpr int HALF = kHalf<D, W>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[4 * HALF];
   lds_u8* const smem = (lds_u8*)smem_raw;
 
   const int G = 1 << lgG;
@@ -225,7 +237,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int rb = CAUSAL ? (nrb - 1 - bid / nbh) : (bid / nbh);
   const int bh = bid % nbh;
   const int b = bh / Hk, hk = bh % Hk;
-  const int row0 = rb * kBM;
+  const int row0 = rb * kBMW;
   const int TG = T << lgG;
   const int tb = row0 >> lgG;  // the workgroup's first token
 
@@ -244,8 +256,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     g.kd = raw_rsrc(kd + slab0, dr);
     g.vd = raw_rsrc(vd + slab0, dr);
   }
-  LaneOffs<D> lo;
-  init_offsets<D>(lo, lane, wave, g.key_bytes);
+  LaneOffs<D, W> lo;
+  init_offsets<D, W>(lo, lane, wave, g.key_bytes);
 
   const int wrow0 = row0 + wave * kRowsPerWave;
   const int my_row = wrow0 + r;
@@ -254,7 +266,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int my_g = my_row & (G - 1);
   const int wt0 = wrow0 >> lgG;                                    // wave's first token
   const int wt1 = (min(wrow0 + kRowsPerWave, TG) - 1) >> lgG;      // wave's last valid token
-  const int blk_last = (min(row0 + kBM, TG) - 1) >> lgG;           // block's last valid token
+  const int blk_last = (min(row0 + kBMW, TG) - 1) >> lgG;           // block's last valid token
   const int kv_end = CAUSAL ? blk_last + 1 : T;
   const int ns = (kv_end + kBN - 1) / kBN;                         // sequence tiles
   const int nchunk = DEPTH ? (L + kDepthRowsPerWave - 1) / kDepthRowsPerWave : 1;  // 16-slot chunks per token
@@ -289,7 +301,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // hidden from the optimiser so that their address adds stay in place
   // instead of becoming hoisted copies of every offset.
   auto buf_of = [&](int pos) -> lds_u8* {
-    return smem + opaque_s((pos & 1) * (2 * TL::BYTES));
+    return smem + opaque_s((pos & 1) * (2 * HALF));
   };
 
   // ---- tile pipeline ------------------------------------------------------------
@@ -310,17 +322,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   auto seq_step = [&](auto parity, auto maskc, int s_end, int d) __attribute__((always_inline)) {
     constexpr int P = decltype(parity)::value;
     constexpr bool MASK = decltype(maskc)::value != 0;
-    lds_u8* const nxt = smem + opaque_s((1 - P) * (2 * TL::BYTES));
+    lds_u8* const nxt = smem + opaque_s((1 - P) * (2 * HALF));
     publish_tile();
     if (sq + 1 < s_end || (d >= nd && sq + 1 < ns))
-      dma_seq<D>(kb, vb, seq_range, g.key_bytes, Hk, sq + 1, nxt, wave, lo);
+      dma_seq<D, W>(kb, vb, seq_range, g.key_bytes, Hk, sq + 1, nxt, wave, lo);
     else if (DEPTH && d < nd)
-      dma_depth<D>(g, d, nchunk, nxt, wave, lane);
+      dma_depth<D, W>(g, d, nchunk, nxt, wave, lane);
     const int kt0 = sq * kBN;
     ++sq;
     ++pos;
     if (MASK && CAUSAL && kt0 > wt1) return;  // nothing visible to this wave
-    seq_tile<D, MASK, CAUSAL>(st, qf, tile_addr<D>(smem + P * (2 * TL::BYTES), lo), kt0, T, my_t, half,
+    seq_tile<D, MASK, CAUSAL>(st, qf, tile_addr<D, W>(smem + P * (2 * HALF), lo), kt0, T, my_t, half,
                               scale_log2);
   };
   // Sequence tiles sq .. s_end - 1 in pairs (buffer 0, then buffer 1), after
@@ -336,9 +348,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     if (sq < s_end) seq_step(P0(), maskc, s_end, d);
   };
   if (DEPTH && nd > 0 && n_int / max(nd, 1) == 0)
-    dma_depth<D>(g, 0, nchunk, smem, wave, lane);
+    dma_depth<D, W>(g, 0, nchunk, smem, wave, lane);
   else
-    dma_seq<D>(kb, vb, seq_range, g.key_bytes, Hk, 0, smem, wave, lo);
+    dma_seq<D, W>(kb, vb, seq_range, g.key_bytes, Hk, 0, smem, wave, lo);
 
   if constexpr (DEPTH) {
     for (int d = 0; d < nd; ++d) {
@@ -350,14 +362,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       publish_tile();
       if (d + 1 < nd) {
         if (sq < ((d + 2) * n_int) / nd)
-          dma_seq<D>(kb, vb, seq_range, g.key_bytes, Hk, sq, nxt, wave, lo);
+          dma_seq<D, W>(kb, vb, seq_range, g.key_bytes, Hk, sq, nxt, wave, lo);
         else
-          dma_depth<D>(g, d + 1, nchunk, nxt, wave, lane);
+          dma_depth<D, W>(g, d + 1, nchunk, nxt, wave, lane);
       } else if (sq < ns) {
-        dma_seq<D>(kb, vb, seq_range, g.key_bytes, Hk, sq, nxt, wave, lo);
+        dma_seq<D, W>(kb, vb, seq_range, g.key_bytes, Hk, sq, nxt, wave, lo);
       }
       ++pos;
-      const TileAddr<D> ta = tile_addr<D>(cur, lo);
+      const TileAddr<D> ta = tile_addr<D, W>(cur, lo);
       const f32x16 sacc = qk_block<D>(qf, ta.k, 32 * dj * TL::ROW_BYTES);
       const int dtok = d / nchunk;
       const int slot0 = (d - dtok * nchunk) * kDepthRowsPerWave;
@@ -396,15 +408,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
 }
 
-template <int D, bool DEPTH, bool CAUSAL>
+template <int D, bool DEPTH, bool CAUSAL, int W>
 hipError_t launch(const FwdArgs& a) {
   const int lgG = __builtin_ctz(a.Hq / a.Hk);
   const int TG = a.T * (a.Hq / a.Hk);
-  const int nrb = (TG + kBM - 1) / kBM;
+  const int nrb = (TG + kBM<W> - 1) / kBM<W>;
   const int64_t nblocks = static_cast<int64_t>(nrb) * a.B * a.Hk;
   const float scale_log2 = kLog2e / sqrtf(static_cast<float>(D));
-  hipLaunchKernelGGL((moda_fwd_bf16_kernel<D, DEPTH, CAUSAL>), dim3(static_cast<unsigned>(nblocks)),
-                     dim3(kThreads), 0, static_cast<hipStream_t>(a.stream),
+  hipLaunchKernelGGL((moda_fwd_bf16_kernel<D, DEPTH, CAUSAL, W>), dim3(static_cast<unsigned>(nblocks)),
+                     dim3(W * 64), 0, static_cast<hipStream_t>(a.stream),
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.kd),
                      static_cast<const uint16_t*>(a.vd), a.B, a.T, a.Hq, a.Hk, a.L, a.Lcap, lgG, nrb, scale_log2,
@@ -412,19 +424,25 @@ hipError_t launch(const FwdArgs& a) {
   return hipGetLastError();
 }
 
+template <int D, int W>
+hipError_t launch_dw(const FwdArgs& a) {
+  if (a.L > 0) return a.causal ? launch<D, true, true, W>(a) : launch<D, true, false, W>(a);
+  return a.causal ? launch<D, false, true, W>(a) : launch<D, false, false, W>(a);
+}
+
 template <int D>
 hipError_t launch_d(const FwdArgs& a) {
-  if (a.L > 0) return a.causal ? launch<D, true, true>(a) : launch<D, true, false>(a);
-  return a.causal ? launch<D, false, true>(a) : launch<D, false, false>(a);
+  return waves_for(a.T) == 8 ? launch_dw<D, 8>(a) : launch_dw<D, 4>(a);
 }
 
 }  // namespace
 
-int fwd_bf16_rows_per_block() { return kBM; }
+int fwd_bf16_rows_per_block(int T) { return waves_for(T) * kRowsPerWave; }
 
 int64_t fwd_bf16_grid_blocks(int B, int T, int Hq, int Hk) {
   const int64_t TG = static_cast<int64_t>(T) * (Hq / Hk);
-  return (TG + kBM - 1) / kBM * B * Hk;
+  const int bm = fwd_bf16_rows_per_block(T);
+  return (TG + bm - 1) / bm * B * Hk;
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a) { return a.d == 64 ? launch_d<64>(a) : launch_d<128>(a); }

@@ -61,12 +61,14 @@ def full_parity(shape, seed, depth_aligned=False):
 
 def sample_rows(shape, n_uniform=24, seed=0):
     """Stratified rows (b, t, h): sequence ends, both edges of the first and last four
-    128-row query blocks (128/G tokens each), and seeded-uniform tokens, per (b, h)."""
+    128-row and 256-row query blocks (128/G and 256/G tokens each: the forward's
+    workgroup sizes), and seeded-uniform tokens, per (b, h)."""
     T, G = shape.T, shape.G
-    tb = max(1, 128 // G)
     special = {0, 1, 2, 3, T - 2, T - 1}
-    for i in range(4):
-        special |= {i * tb, i * tb + tb - 1, T - (i + 1) * tb, T - i * tb - 1}
+    for rows in (128, 256):
+        tb = max(1, rows // G)
+        for i in range(4):
+            special |= {i * tb, i * tb + tb - 1, T - (i + 1) * tb, T - i * tb - 1}
     special = sorted(t for t in special if 0 <= t < T)
     rng = np.random.default_rng(seed)
     rows = []

@@ -7,7 +7,7 @@ import torch
 
 import oracle
 from depth_stream_attention_amd import inputs as I
-from parity_util import BF16_MAX, check, full_parity, run_path, sample_rows, sampled_parity, say
+from parity_util import BF16_MAX, check, full_parity, run_path, sample_rows, sampled_parity, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -46,6 +46,40 @@ def test_workload4(v):
 @pytest.mark.parametrize("v", [0, 1])
 def test_workload5(v):
     _run(5, v, n_uniform=16)
+
+
+# Sequences of 32768 tokens and more run the forward's 8-wave workgroups (256 rows,
+# 128-row depth tiles); these shapes cover that kernel for both head dims, G from 1
+# to 32, causal and full attention, a ragged length and depth counts that leave a
+# partial 16-slot chunk.
+LONG_SHAPES = [
+    I.Shape(1, 32768, 2, 2, 64, 0),
+    I.Shape(1, 32768, 4, 1, 128, 5),
+    I.Shape(1, 32771, 8, 2, 128, 16),
+    I.Shape(1, 32768, 32, 1, 64, 33, causal=False),
+    I.Shape(2, 32768, 4, 2, 128, 48),
+]
+
+
+@pytest.mark.parametrize("i", range(len(LONG_SHAPES)))
+def test_long_sequence_workgroups(i):
+    shape = LONG_SHAPES[i]
+    say("long-sequence shape", shape.describe())
+    dev = to_dev(I.random_inputs(shape, 400 + i))
+    out, lse = run_path(shape, dev)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    rows = sample_rows(shape, n_uniform=8, seed=400 + i)
+    sampled_parity(shape, dev, out, lse, rows, "long %d" % i)
+
+
+def test_long_sequence_depth_aligned():
+    """The depth-aligned stress (every depth slot of a lead head near its query) on the
+    8-wave kernel, sampled on late rows."""
+    shape = I.Shape(1, 32768, 8, 2, 128, 40)
+    dev = to_dev(I.random_inputs(shape, 420, depth_aligned=True))
+    out, lse = run_path(shape, dev)
+    rows = _late_rows(shape, 420, n_uniform=8)
+    sampled_parity(shape, dev, out, lse, rows, "long depth-aligned")
 
 
 def _late_rows(shape, seed, n_uniform=16):
