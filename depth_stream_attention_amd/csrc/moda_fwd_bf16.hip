@@ -63,8 +63,11 @@ template <int D, int W>
 constexpr int kNX = Tile<D>::CH / W;  // sequence-tile loads per wave per matrix
 template <int D>
 constexpr int kNXD = kDepthRowsPerWave * Tile<D>::ROW_BYTES / 1024;  // depth-tile loads per wave per matrix
-// An LDS buffer holds K in its first kHalf bytes and V in the next: a depth
-// tile has W * 16 rows, a sequence tile kBN rows (the first Tile::BYTES of each).
+// LDS holds the two pipeline buffers as [K0 | K1 | V0 | V1], each region kHalf
+// bytes (a depth tile has W * 16 rows, a sequence tile kBN rows): buffer P's K
+// starts at P * kHalf and its V at (2 + P) * kHalf.  With the V-region offset
+// folded into the per-lane V read offsets, every read address of either buffer
+// is a per-lane register plus an instruction immediate below 64 KiB.
 template <int D, int W>
 constexpr int kHalf = (W * kDepthRowsPerWave > kBN ? W * kDepthRowsPerWave : kBN) * Tile<D>::ROW_BYTES;
 
@@ -84,7 +87,7 @@ struct Geo {
 };
 
 // Direct-to-LDS loads of depth tile `idx` into `buf` (K at buf, V at
-// buf + kHalf).  For every wave w the tile holds token w*tok_wave + dtok of
+// buf + 2 * kHalf).  For every wave w the tile holds token w*tok_wave + dtok of
 // the workgroup, slots [16*dch, 16*dch + 16), at tile rows [16w, 16w + 16).
 // Instruction x of wave w fills tile rows pr = (w*NXD + x)*RPI + lane/CH,
 // physical chunk pc = lane % CH, with logical chunk pc ^ swz(pr).  Padding
@@ -107,7 +110,7 @@ __device__ __forceinline__ void dma_depth(const Geo& g, int idx, int nchunk, lds
     const uint32_t ov = valid ? row_off + ((pc ^ TL::swz_v(pr)) * 16) : kOutOfRange;
     const uint32_t dk = lds_addr(buf + (wave * kNXD<D> + x) * 1024);
     dma16(g.kd, dk, ok);
-    dma16(g.vd, dk + kHalf<D, W>, ov);
+    dma16(g.vd, dk + 2 * kHalf<D, W>, ov);
   }
 }
 
@@ -135,7 +138,7 @@ __device__ __forceinline__ void init_offsets(LaneOffs<D, W>& lo, int lane, int w
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
     const int lc = (32 * dt + 16 * q) / 8 + ((i & 3) >> 1);  // logical chunk of column d0 + 4*(i%4)
-    lo.vr[dt] = row0 * TL::ROW_BYTES + 8 * (i & 1) + ((lc ^ sw) * 16);
+    lo.vr[dt] = 2 * kHalf<D, W> + row0 * TL::ROW_BYTES + 8 * (i & 1) + ((lc ^ sw) * 16);
   }
   // Load instruction x of wave w fills tile rows pr = (w*NX + x)*RPI + lane/CH,
   // physical chunk pc = lane % CH, with logical chunk pc ^ swz(pr).
@@ -149,7 +152,7 @@ __device__ __forceinline__ void init_offsets(LaneOffs<D, W>& lo, int lane, int w
 }
 
 // Direct-to-LDS loads of sequence tile `idx` into `buf` (K at buf, V at
-// buf + kHalf), through descriptors rebased to the tile's first key (scalar
+// buf + 2 * kHalf), through descriptors rebased to the tile's first key (scalar
 // work), so the per-lane offsets are loop invariant.  Keys past the sequence
 // end fall outside the range and read as zero.
 template <int D, int W>
@@ -165,7 +168,7 @@ __device__ __forceinline__ void dma_seq(const uint16_t* kb, const uint16_t* vb, 
   for (int x = 0; x < kNX<D, W>; ++x) {
     const uint32_t dk = lds_addr(buf + (wave * kNX<D, W> + x) * 1024);
     dma16(rk, dk, lo.dk[x]);
-    dma16(rv, dk + kHalf<D, W>, lo.dv[x]);
+    dma16(rv, dk + 2 * kHalf<D, W>, lo.dv[x]);
   }
 }
 
@@ -183,7 +186,7 @@ __device__ __forceinline__ TileAddr<D> tile_addr(const lds_u8* buf, const LaneOf
 #pragma unroll
   for (int sl = 0; sl < D / 16; ++sl) a.k[sl] = base + lo.kr[sl];
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) a.v[dt] = base + kHalf<D, W> + lo.vr[dt];
+  for (int dt = 0; dt < D / 32; ++dt) a.v[dt] = base + lo.vr[dt];
   return a;
 }
 
@@ -301,7 +304,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   // hidden from the optimiser so that their address adds stay in place
   // instead of becoming hoisted copies of every offset.
   auto buf_of = [&](int pos) -> lds_u8* {
-    return smem + opaque_s((pos & 1) * (2 * HALF));
+    return smem + opaque_s((pos & 1) * HALF);
   };
 
   // ---- tile pipeline ------------------------------------------------------------
@@ -322,7 +325,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   auto seq_step = [&](auto parity, auto maskc, int s_end, int d) __attribute__((always_inline)) {
     constexpr int P = decltype(parity)::value;
     constexpr bool MASK = decltype(maskc)::value != 0;
-    lds_u8* const nxt = smem + opaque_s((1 - P) * (2 * HALF));
+    lds_u8* const nxt = smem + opaque_s((1 - P) * HALF);
     publish_tile();
     if (sq + 1 < s_end || (d >= nd && sq + 1 < ns))
       dma_seq<D, W>(kb, vb, seq_range, g.key_bytes, Hk, sq + 1, nxt, wave, lo);
@@ -332,7 +335,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     ++sq;
     ++pos;
     if (MASK && CAUSAL && kt0 > wt1) return;  // nothing visible to this wave
-    seq_tile<D, MASK, CAUSAL>(st, qf, tile_addr<D, W>(smem + P * (2 * HALF), lo), kt0, T, my_t, half,
+    seq_tile<D, MASK, CAUSAL>(st, qf, tile_addr<D, W>(smem + P * HALF, lo), kt0, T, my_t, half,
                               scale_log2);
   };
   // Sequence tiles sq .. s_end - 1 in pairs (buffer 0, then buffer 1), after
