@@ -9,16 +9,18 @@
 //   * Group-aware rows: for one (batch b, KV head hk), expanded row
 //     i_q = t*G + g is token t, query head hk*G + g.  Consecutive rows of one
 //     token are its G heads, which share every K/V element they read.
-//   * A workgroup owns BM = 128 consecutive expanded rows (128/G tokens) of one
-//     (b, hk); each of its 4 waves owns 32 rows (32/G tokens).  The block's
-//     tokens are [t_start, t_end) with t_start = floor(row0/G) and
+//   * A workgroup of W waves owns BM = 32*W consecutive expanded rows (BM/G
+//     tokens) of one (b, hk); each wave owns 32 rows (32/G tokens).  W = 4 (two
+//     workgroups per CU) for sequences shorter than 32768 tokens, W = 8 (one
+//     per CU, each staged K/V tile serving 256 rows) from there on.  The
+//     block's tokens are [t_start, t_end) with t_start = floor(row0/G) and
 //     t_end = floor(last/G) + 1; sequence keys at or past t_end are never read.
-//   * Every workgroup runs one pipeline of 64-row K/V tiles in LDS, double
-//     buffered.  Tiles are staged by direct-to-LDS buffer loads (16 bytes per
-//     lane, no staging registers): the loads of tile i+1 are issued right
-//     after the barrier that publishes tile i, and each wave waits for its own
-//     loads before the next barrier.  Two kinds of tile:
-//       - sequence tiles of 64 keys, shared by all 4 waves;
+//   * Every workgroup runs one pipeline of K/V tiles in LDS, double buffered.
+//     Tiles are staged by direct-to-LDS buffer loads (16 bytes per lane, no
+//     staging registers) issued as inline asm: the loads of tile i+1 are
+//     issued right after the barrier that publishes tile i, and each wave
+//     waits for its own loads before the next barrier.  Two kinds of tile:
+//       - sequence tiles of 64 keys, shared by all W waves;
 //       - depth tiles: 16 rows per wave, 16 consecutive slots of one of the
 //         wave's own tokens, read from the packed [B][T][Hk][L][d] stream (each
 //         (token, KV head) slab is one contiguous run, each depth element is
