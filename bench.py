@@ -18,6 +18,7 @@ value = forward flops of the L=48 MoDA forward / its average kernel time
 """
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -39,13 +40,21 @@ KERNEL_SRC = os.path.join(ROOT, "depth_stream_attention_amd", "csrc", "moda_fwd_
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "moda_fwd_bf16_long_L48_traffic.json")
 
 
+def _code_text(text):
+    """Source text without comments and blank runs, so that comment edits keep the hash."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def kernel_source_hash():
-    """Hash of the forward kernel's sources and its build flags (the counters describe one binary)."""
+    """Hash of the forward kernel's code (sources without comments) and its build flags: the
+    counters describe one binary."""
     from depth_stream_attention_amd import build as pkg_build
     h = hashlib.sha256()
     for name in ("moda_fwd_bf16.hip", "moda_tile.h", "moda_device.h"):
-        with open(os.path.join(ROOT, "depth_stream_attention_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "depth_stream_attention_amd", "csrc", name), encoding="utf-8") as f:
+            h.update(_code_text(f.read()).encode())
     flags = [f for f in pkg_build.HIPCC_FLAGS if not f.startswith("-I")]  # include paths vary by checkout
     h.update(" ".join(flags + pkg_build.SOURCE_FLAGS.get("moda_fwd_bf16.hip", [])).encode())
     return h.hexdigest()[:16]
