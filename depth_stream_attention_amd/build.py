@@ -42,15 +42,23 @@ def _hipcc():
     raise RuntimeError("hipcc not found")
 
 
+def device_listing(src: str) -> str:
+    """Path of the gfx950 assembly that build() keeps for the .hip source `src`."""
+    return os.path.join(BUILD_DIR, os.path.splitext(src)[0] + "-hip-amdgcn-amd-amdhsa-gfx950.s")
+
+
 def build(verbose: bool = False, extra_flags=()) -> str:
     """Compile every source for gfx950 and link libmoda.so (and the measurement library
-    libmoda_probe.so) next to this file."""
+    libmoda_probe.so) next to this file.  The device assembly of each .hip source is kept
+    (-save-temps) and checked for the inline-asm load hazard of asm_check before linking."""
+    from . import asm_check
+
     hipcc = _hipcc()
     os.makedirs(BUILD_DIR, exist_ok=True)
 
     def compile_one(src):
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-        lang = ["-x", "hip"] if src.endswith(".hip") else []
+        lang = ["-x", "hip", "-save-temps=obj"] if src.endswith(".hip") else []
         cmd = ([hipcc] + HIPCC_FLAGS + SOURCE_FLAGS.get(src, []) + list(extra_flags) + lang +
                ["-c", os.path.join(CSRC, src), "-o", obj])
         if verbose:
@@ -62,6 +70,12 @@ def build(verbose: bool = False, extra_flags=()) -> str:
             raise RuntimeError("hipcc failed on %s:\n%s" % (src, err))
         if verbose and err.strip():
             print(err, file=sys.stderr)
+        if src.endswith(".hip"):
+            with open(device_listing(src)) as f:
+                bad = asm_check.check_listing(f.read())
+            if bad:
+                raise RuntimeError("%s: direct-to-LDS load hazard in the compiled code:\n%s" %
+                                   (src, "\n".join("%s: %s" % b for b in bad[:10])))
         return obj
 
     with ThreadPoolExecutor(max_workers=4) as ex:

@@ -66,9 +66,15 @@ __device__ __forceinline__ u32x4 raw_rsrc(const uint16_t* base, uint32_t bytes) 
 // transposed LDS read (a builtin) wait for all such loads first -- in a double
 // buffered pipeline that is the next tile's load, in the middle of the current
 // tile.  Visibility is the pipeline's own explicit vmcnt wait and barrier.
-// The s_nop covers the M0 write -> LDS-DMA hazard (the compiler sets M0 just
-// before the statement).  rsrc and lds are scalar operands: they must be the
-// same in every lane of the wave.
+// The compiler's hazard checks do not look inside inline asm.  The s_nop
+// covers the M0 write -> LDS-DMA hazard (the compiler sets M0 just before the
+// statement).  The other hazard of the statement, a VALU write of a descriptor
+// SGPR fewer than 5 wait states before it (the compiler reloads spilled SGPRs
+// with v_readlane; read early, a descriptor dword is stale and the load goes
+// to a wrong address), is left to the surrounding code: the build scans the
+// compiled kernels for it and refuses to link a library that has it.  rsrc
+// and lds are scalar operands: they must be the same in every lane of the
+// wave.
 __device__ __forceinline__ void dma16(const u32x4& rsrc, uint32_t lds, uint32_t voff) {
   asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
 }

@@ -9,37 +9,28 @@ that sets each load's LDS address needs its wait state from the asm itself.
 This compiles the sources to gfx950 assembly as the library build does and
 checks, in every kernel that issues such loads:
   - each one is preceded inside its asm block by s_nop (M0 -> LDS-DMA hazard);
+  - no VALU instruction writes one of its descriptor SGPRs fewer than 5 wait
+    states before it (a vector memory instruction reads an SGPR correctly only
+    5 wait states after a VALU write; under SGPR pressure the compiler reloads
+    descriptors from VGPR lanes with v_readlane just before the statement, and
+    a stale descriptor dword sends the load to a wrong address).  A branch
+    target or the kernel start inside that window counts as a violation.  The
+    check is asm_check's, which the build also runs on every kernel before it
+    links the library;
   - each s_barrier follows an s_waitcnt with vmcnt(0), with no vector memory
     instruction and no branch target in between (the tile pipeline's publish
     step: all of the wave's loads have landed before the barrier)."""
 import os
-import re
 import shutil
 import subprocess
 
 import pytest
 
 from depth_stream_attention_amd import build as B
+from depth_stream_attention_amd.asm_check import functions, sgpr_hazards
 
 pytestmark = pytest.mark.skipif(shutil.which(B._hipcc()) is None and not os.path.exists(B._hipcc()),
                                 reason="needs hipcc")
-
-_FUNC = re.compile(r"^(_Z\S+):")
-
-
-def functions(asm_text):
-    """{name: [lines]} of the kernels in one assembly listing."""
-    out, cur = {}, None
-    for line in asm_text.split("\n"):
-        m = _FUNC.match(line)
-        if m:
-            cur = m.group(1)
-            out[cur] = []
-        elif cur is not None:
-            out[cur].append(line)
-            if line.strip().startswith("s_endpgm"):
-                cur = None
-    return out
 
 
 def scan(lines):
@@ -94,6 +85,7 @@ def test_asm_lds_loads_are_published(tmp_path, src, kernel):
     for name, lines in funcs.items():
         n, bad = scan(lines)
         assert n > 0, "%s: no inline-asm LDS loads found: the check is looking at the wrong code" % name
+        bad += sgpr_hazards(lines)
         assert not bad, name + "\n" + "\n".join(bad[:10])
 
 
@@ -136,3 +128,22 @@ def test_functions_splits_kernels():
     text = "\n".join(["_Z1av:", "s_nop 0", "s_endpgm", "_Z1bv:  ; comment", "s_barrier", "s_endpgm"])
     f = functions(text)
     assert list(f) == ["_Z1av", "_Z1bv"] and f["_Z1bv"][0] == "s_barrier"
+
+
+def test_hazard_check_flags_a_descriptor_read_too_soon():
+    lines = ["v_readlane_b32 s27, v223, 41", "v_cndmask_b32_e32 v72, v69, v72, vcc", "s_mov_b32 m0, s50",
+             ";;#ASMSTART", "s_nop 0", "buffer_load_dwordx4 v72, s[24:27], 0 offen lds", ";;#ASMEND"]
+    bad = sgpr_hazards(lines)
+    assert len(bad) == 1 and "v_readlane_b32 s27" in bad[0] and "3 wait states" in bad[0]
+
+
+def test_hazard_check_accepts_five_wait_states():
+    lines = ["v_readlane_b32 s27, v223, 41", "s_mov_b32 m0, s50",
+             ";;#ASMSTART", "s_nop 4", "buffer_load_dwordx4 v72, s[24:27], 0 offen lds", ";;#ASMEND"]
+    assert sgpr_hazards(lines) == []
+
+
+def test_hazard_check_ignores_other_sgprs_and_flags_labels():
+    ok = ["s_nop 4", "v_readlane_b32 s30, v1, 0", "s_nop 0", "buffer_load_dwordx4 v2, s[24:27], 0 offen lds"]
+    assert sgpr_hazards(ok) == []
+    assert len(sgpr_hazards([".LBB0_1:", "s_nop 0", "buffer_load_dwordx4 v2, s[4:7], 0 offen lds"])) == 1
