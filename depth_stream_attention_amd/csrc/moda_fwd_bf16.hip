@@ -314,8 +314,9 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   // end) are unmasked for every wave; the few after them overlap the
   // workgroup's own tokens and take the masked path.  The nd depth tiles are
   // spread evenly among the unmasked ones -- depth tile d follows sequence
-  // tile (d+1)*n_int/nd - 1 -- so each depth load (a once-read HBM stream) is
-  // prefetched under a full sequence tile of MFMA work.  Every loop body is
+  // tile s_end(d) - 1, about (d+1)*n_int/nd - 1 -- so each depth load (a
+  // once-read HBM stream) is prefetched under a full sequence tile of MFMA
+  // work.  Every loop body is
   // straight-line per wave, so the accumulator keeps its registers.
   const int n_int = CAUSAL ? min(ns, (tb + 1) / kBN) : T / kBN;
   int pos = 0;  // pipeline position: selects the LDS buffer
@@ -352,21 +353,28 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     }
     if (sq < s_end) seq_step(P0(), maskc, s_end, d);
   };
-  if (DEPTH && nd > 0 && n_int / max(nd, 1) == 0)
+  // Depth tile d follows sequence tile s_end(d) - 1.  Each workgroup shifts its
+  // schedule earlier by its own fraction (one of 64, from a hash of the
+  // workgroup id) of the depth-tile spacing: workgroups that run at the same
+  // time have nearly equal n_int and nd and would otherwise issue their depth
+  // loads, each a burst of HBM reads, in the same steps.
+  const int d_off = (static_cast<int>((static_cast<uint32_t>(bid) * 2654435761u) >> 26) * n_int) >> 6;
+  auto s_end_of = [&](int d) { return ((d + 1) * n_int - d_off) / max(nd, 1); };
+  if (DEPTH && nd > 0 && s_end_of(0) == 0)
     dma_depth<D, W>(g, 0, nchunk, smem, wave, lane);
   else
     dma_seq<D, W>(kb, vb, seq_range, g.key_bytes, Hk, 0, smem, wave, lo);
 
   if constexpr (DEPTH) {
     for (int d = 0; d < nd; ++d) {
-      const int s_end = ((d + 1) * n_int) / nd;
+      const int s_end = s_end_of(d);
       seq_run(std::integral_constant<int, 0>(), s_end, d);
       // depth tile d: each wave sees only its own token's slots
       lds_u8* cur = buf_of(pos);
       lds_u8* nxt = buf_of(pos + 1);
       publish_tile();
       if (d + 1 < nd) {
-        if (sq < ((d + 2) * n_int) / nd)
+        if (sq < s_end_of(d + 1))
           dma_seq<D, W>(kb, vb, seq_range, g.key_bytes, Hk, sq, nxt, wave, lo);
         else
           dma_depth<D, W>(g, d + 1, nchunk, nxt, wave, lane);
