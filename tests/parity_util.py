@@ -14,6 +14,28 @@ F32_MAX = 1e-4
 BF16_LSE, F32_LSE = 1e-3, 1e-4
 
 
+def random_shapes(n, seed, budget):
+    """n forward shapes drawn with a fixed seed, each with a flag for depth-aligned inputs:
+    every group size, both head dims, causal and full attention, ragged lengths, L from 0
+    past a 16-slot chunk boundary; the oracle's work B*Hq*T*(T/2+L)*d stays under
+    `budget` multiply-adds per case."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        G = int(rng.choice([1, 2, 4, 8, 16, 32]))
+        Hk = int(rng.choice([1, 2, 4]))
+        d = int(rng.choice([64, 128]))
+        B = int(rng.integers(1, 4))
+        T = int(rng.integers(1, 700))
+        L = int(rng.choice([0, int(rng.integers(1, 70))]))
+        causal = bool(rng.random() < 0.75)
+        aligned = bool(L > 0 and rng.random() < 0.3)
+        if B * Hk * G * T * (T / 2 + L) * d > budget:
+            continue
+        out.append((I.Shape(B, T, Hk * G, Hk, d, L, causal=causal), aligned))
+    return out
+
+
 def say(*a):
     print(*a, flush=True)
 

@@ -14,7 +14,7 @@ import torch
 import oracle
 from depth_stream_attention_amd import api
 from depth_stream_attention_amd import inputs as I
-from parity_util import say
+from parity_util import random_shapes, say
 
 pytestmark = pytest.mark.gpu
 S = I.Shape
@@ -112,3 +112,8 @@ def test_bwd_is_deterministic_and_reuses_workspace():
     b = run_bwd(shape, host, dout, workspace=ws)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("i,case", list(enumerate(random_shapes(12, 2029, 4e8))))
+def test_bwd_random_shapes(i, case):
+    bwd_case(case[0], 1500 + i)

@@ -10,7 +10,7 @@ import torch
 import oracle
 from depth_stream_attention_amd import api
 from depth_stream_attention_amd import inputs as I
-from parity_util import full_parity, run_path, say, to_dev
+from parity_util import full_parity, random_shapes, run_path, say, to_dev
 
 pytestmark = pytest.mark.gpu
 S = I.Shape
@@ -137,3 +137,11 @@ def test_binding_rejects_bad_tensors():
         api.moda_attn_fwd(q, kv, kv)
     assert e.value.code == api.MODA_ERR_UNSUPPORTED
     say("binding errors ok")
+
+
+# ---- seeded random shapes ---------------------------------------------------------
+
+@pytest.mark.parametrize("i,case", list(enumerate(random_shapes(24, 2027, 1e9))))
+def test_random_shapes(i, case):
+    shape, aligned = case
+    full_parity(shape, 500 + i, depth_aligned=aligned)
