@@ -138,3 +138,30 @@ def test_depth_aligned_full_size(c, v):
     say("depth-aligned %d.%d: previous-slab mistake moves lead-head rows by %.3g .. %.3g (n=%d)"
         % (c, v, gap.min(), gap.max(), gap.size))
     assert gap.size > 0 and gap.min() > 10 * BF16_MAX, "the stress input does not expose a wrong depth slab"
+
+
+def _random_long_shapes(n, seed):
+    """n shapes of 32768 to 36000 tokens (the 8-wave kernel) drawn with a fixed seed:
+    group sizes 1 to 32, both head dims, causal and full attention, L from 0 to 64."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        G = int(rng.choice([1, 2, 4, 8, 16, 32]))
+        Hk = int(rng.choice([1, 2]))
+        d = int(rng.choice([64, 128]))
+        T = int(rng.integers(32768, 36001))
+        L = int(rng.choice([0, int(rng.integers(1, 65))]))
+        causal = bool(rng.random() < 0.75)
+        out.append(I.Shape(1, T, Hk * G, Hk, d, L, causal=causal))
+    return out
+
+
+@pytest.mark.parametrize("i,shape", list(enumerate(_random_long_shapes(6, 2031))))
+def test_random_long_shapes(i, shape):
+    say("random long shape", shape.describe())
+    aligned = shape.L > 0 and i % 2 == 0
+    dev = to_dev(I.random_inputs(shape, 700 + i, depth_aligned=aligned))
+    out, lse = run_path(shape, dev)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    rows = _late_rows(shape, 700 + i, n_uniform=6) if aligned else sample_rows(shape, n_uniform=6, seed=700 + i)
+    sampled_parity(shape, dev, out, lse, rows, "random long %d" % i)
