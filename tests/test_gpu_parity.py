@@ -37,7 +37,7 @@ def test_ragged_lengths(T):
     full_parity(S(1, T, 8, 2, 128, 3), 20 + T)
 
 
-@pytest.mark.parametrize("L", [0, 1, 31, 32, 33, 96])
+@pytest.mark.parametrize("L", [0, 1, 31, 32, 33, 96, 257, 512])
 def test_depth_slot_counts(L):
     full_parity(S(2, 97, 8, 2, 128, L), 30 + L)
 
