@@ -44,6 +44,18 @@ def _sgprs(tok):
     return set(range(int(m.group(1)), int(m.group(2)) + 1))
 
 
+def _sgpr_dests(text):
+    """SGPRs a VALU instruction writes: its first operand (v_readlane, v_readfirstlane,
+    v_cmp), and for the forms with a scalar carry or condition output (v_*_co_*,
+    v_div_scale_*, v_mad_u64_u32, v_mad_i64_i32) also its second."""
+    op, _, rest = text.partition(" ")
+    ops = [o.strip() for o in rest.split(",")]
+    out = _sgprs(ops[0]) if ops else set()
+    if len(ops) > 1 and ("_co_" in op or "div_scale" in op or op.startswith(("v_mad_u64", "v_mad_i64"))):
+        out |= _sgprs(ops[1])
+    return out
+
+
 def is_lds_load(text):
     t = text.strip().split(";")[0].strip()
     return t.startswith("buffer_load") and t.endswith(" lds")
@@ -72,7 +84,7 @@ def sgpr_hazards(lines, need=VMEM_SGPR_WAIT_STATES):
             if not u or u.startswith("."):
                 continue
             op = u.split()[0]
-            if op.startswith("v_") and " " in u and _sgprs(u.split(None, 1)[1].split(",")[0]) & rsrc:
+            if op.startswith("v_") and " " in u and _sgpr_dests(u) & rsrc:
                 bad.append("line %d: %s written by '%s' %d wait states before: %s" % (i, sorted(rsrc), u, ws, t))
                 break
             ws += int(u.split()[1], 0) + 1 if op == "s_nop" else 1

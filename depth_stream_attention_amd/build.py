@@ -51,7 +51,10 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     """Compile every source for gfx950 and link libmoda.so (and the measurement library
     libmoda_probe.so) next to this file.  The device assembly of each .hip source is kept
     (-save-temps) and checked for the inline-asm load hazard of asm_check before linking."""
-    from . import asm_check
+    try:
+        from . import asm_check
+    except ImportError:  # run as a script
+        import asm_check
 
     hipcc = _hipcc()
     os.makedirs(BUILD_DIR, exist_ok=True)

@@ -147,3 +147,10 @@ def test_hazard_check_ignores_other_sgprs_and_flags_labels():
     ok = ["s_nop 4", "v_readlane_b32 s30, v1, 0", "s_nop 0", "buffer_load_dwordx4 v2, s[24:27], 0 offen lds"]
     assert sgpr_hazards(ok) == []
     assert len(sgpr_hazards([".LBB0_1:", "s_nop 0", "buffer_load_dwordx4 v2, s[4:7], 0 offen lds"])) == 1
+
+
+def test_hazard_check_sees_scalar_carry_outputs():
+    lines = ["v_add_co_u32_e64 v1, s[26:27], v2, v3", "s_nop 0",
+             "buffer_load_dwordx4 v2, s[24:27], 0 offen lds"]
+    bad = sgpr_hazards(lines)
+    assert len(bad) == 1 and "v_add_co_u32_e64" in bad[0]
