@@ -30,13 +30,13 @@ int validate_fwd(bool bf16, const void* q, const void* k, const void* v, const v
   if (!is_pow2_in(G, 1, 32)) return MODA_ERR_UNSUPPORTED;
   // Launch-size limits of this build: expanded rows and workgroup counts in int32.
   if (static_cast<int64_t>(T) * G > INT_MAX / 2) return MODA_ERR_UNSUPPORTED;
-  if (moda::fwd_bf16_grid_blocks(B, T, Hq, Hk) > INT_MAX || moda::fwd_f32_grid_blocks(B, T, Hq) > INT_MAX)
+  if (moda::fwd_bf16_grid_blocks(B, T, Hq, Hk, d) > INT_MAX || moda::fwd_f32_grid_blocks(B, T, Hq) > INT_MAX)
     return MODA_ERR_UNSUPPORTED;
   // The bf16 kernel addresses one (batch, KV head) sequence and one
   // workgroup's depth slabs (at most one token per expanded row of the
   // workgroup) with 32-bit byte offsets.
   if (bf16 && (static_cast<int64_t>(T + 64) * Hk * d * 2 >= (int64_t{1} << 31) ||
-               static_cast<int64_t>(moda::fwd_bf16_rows_per_block(T) + 1) * Hk * Lcap * d * 2 >=
+               static_cast<int64_t>(moda::fwd_bf16_rows_per_block(T, d) + 1) * Hk * Lcap * d * 2 >=
                    (int64_t{1} << 31)))
     return MODA_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse)) return MODA_ERR_ALIGN;

@@ -10,9 +10,10 @@
 //     i_q = t*G + g is token t, query head hk*G + g.  Consecutive rows of one
 //     token are its G heads, which share every K/V element they read.
 //   * A workgroup of W waves owns BM = 32*W consecutive expanded rows (BM/G
-//     tokens) of one (b, hk); each wave owns 32 rows (32/G tokens).  W = 4 (two
-//     workgroups per CU) for sequences shorter than 32768 tokens, W = 8 (one
-//     per CU, each staged K/V tile serving 256 rows) from there on.  The
+//     tokens) of one (b, hk); each wave owns 32 rows (32/G tokens).  With
+//     d = 128, W = 4 (two workgroups per CU) for sequences shorter than 32768
+//     tokens, W = 8 (one per CU, each staged K/V tile serving 256 rows) from
+//     there on; with d = 64, W = 4 at three or four workgroups per CU.  The
 //     block's tokens are [t_start, t_end) with t_start = floor(row0/G) and
 //     t_end = floor(last/G) + 1; sequence keys at or past t_end are never read.
 //   * Every workgroup runs one pipeline of K/V tiles in LDS, double buffered.
@@ -54,10 +55,16 @@ constexpr int kRowsPerWave = 32;
 // W waves per workgroup (4, or 8 for long sequences): W * 32 expanded rows.
 template <int W>
 constexpr int kBM = W * kRowsPerWave;
-// Sequences at least this long run 8-wave workgroups (one per CU), which stage
-// each K/V tile once for 256 rows; shorter ones run two 4-wave workgroups per CU.
+// With d = 128, sequences at least this long run 8-wave workgroups (one per
+// CU), which stage each K/V tile once for 256 rows; shorter ones run two 4-wave
+// workgroups per CU.  With d = 64 the kernel needs few enough registers for
+// three waves per SIMD (four without the depth stage), so every length runs
+// 4-wave workgroups, three (four) per CU.
 constexpr int kLongT = 32768;
-__host__ __device__ constexpr int waves_for(int T) { return T >= kLongT ? 8 : 4; }
+__host__ __device__ constexpr int waves_for(int T, int d) { return (d == 128 && T >= kLongT) ? 8 : 4; }
+// Waves per SIMD the kernel is compiled for (its register budget).
+template <int D, int W, bool DEPTH>
+constexpr int kWavesPerEU = (D == 64 && W == 4) ? (DEPTH ? 3 : 4) : 2;
 constexpr int kDepthRowsPerWave = 16;                     // slots of one token per wave in a depth tile
 
 // Direct-to-LDS load instructions per wave per K (or V) tile.
@@ -223,7 +230,7 @@ __device__ __forceinline__ void seq_tile(RowState<D>& st, const bf16x8 (&qf)[D /
 }
 
 template <int D, bool DEPTH, bool CAUSAL, int W>
-__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void moda_fwd_bf16_kernel(
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(kWavesPerEU<D, W, DEPTH>, kWavesPerEU<D, W, DEPTH>))) void moda_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ kd, const uint16_t* __restrict__ vd, int B, int T, int Hq, int Hk, int L,
     int Lcap, int lgG, int nrb, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
@@ -445,16 +452,19 @@ hipError_t launch_dw(const FwdArgs& a) {
 
 template <int D>
 hipError_t launch_d(const FwdArgs& a) {
-  return waves_for(a.T) == 8 ? launch_dw<D, 8>(a) : launch_dw<D, 4>(a);
+  if constexpr (D == 128) {
+    if (waves_for(a.T, D) == 8) return launch_dw<D, 8>(a);
+  }
+  return launch_dw<D, 4>(a);
 }
 
 }  // namespace
 
-int fwd_bf16_rows_per_block(int T) { return waves_for(T) * kRowsPerWave; }
+int fwd_bf16_rows_per_block(int T, int d) { return waves_for(T, d) * kRowsPerWave; }
 
-int64_t fwd_bf16_grid_blocks(int B, int T, int Hq, int Hk) {
+int64_t fwd_bf16_grid_blocks(int B, int T, int Hq, int Hk, int d) {
   const int64_t TG = static_cast<int64_t>(T) * (Hq / Hk);
-  const int bm = fwd_bf16_rows_per_block(T);
+  const int bm = fwd_bf16_rows_per_block(T, d);
   return (TG + bm - 1) / bm * B * Hk;
 }
 

@@ -49,8 +49,8 @@ struct KvProjArgs {
 
 hipError_t launch_fwd_bf16(const FwdArgs& a);
 hipError_t launch_fwd_f32(const FwdArgs& a);
-int64_t fwd_bf16_grid_blocks(int B, int T, int Hq, int Hk);
-int fwd_bf16_rows_per_block(int T);  // expanded query rows per workgroup of the bf16 forward at length T
+int64_t fwd_bf16_grid_blocks(int B, int T, int Hq, int Hk, int d);
+int fwd_bf16_rows_per_block(int T, int d);  // expanded query rows per workgroup of the bf16 forward
 int64_t fwd_f32_grid_blocks(int B, int T, int Hq);
 
 hipError_t launch_decode_bf16(const DecodeArgs& a);

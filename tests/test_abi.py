@@ -61,12 +61,14 @@ def test_fwd_validation(lib, name):
         assert f(T=(1 << 22), Hq=16, Hk=8) == U
         assert f(L=1024, Hq=64, Hk=64) == U
         # A workgroup's depth window spans (rows per workgroup + 1) * Hk * L * d * 2 bytes:
-        # 128 rows below 32768 tokens, 256 from there on.  Hk=8, d=128, L=4081 fits the
-        # 32-bit offsets with 128 rows (1.08e9 bytes) but not with 256 (2.148e9 > 2^31).  A
-        # misaligned lse makes the accepted shape stop at the (later) alignment check,
-        # so nothing is launched with these placeholder pointers.
+        # with d=128, 128 rows below 32768 tokens and 256 from there on; with d=64, 128
+        # rows at every length.  Hk=8, d=128, L=4081 fits the 32-bit offsets with 128 rows
+        # (1.08e9 bytes) but not with 256 (2.148e9 > 2^31); Hk=8, d=64, L=8162 is the same
+        # byte count.  A misaligned lse makes the accepted shape stop at the (later)
+        # alignment check, so nothing is launched with these placeholder pointers.
         assert f(T=32767, Hq=8, Hk=8, L=4081, lse=MIS) == AL
         assert f(T=32768, Hq=8, Hk=8, L=4081, lse=MIS) == U
+        assert f(T=32768, Hq=8, Hk=8, d=64, L=8162, lse=MIS) == AL
 
 
 def test_layout_validation(lib):
