@@ -551,11 +551,11 @@ def workloads_leg(iters=8):
 
 
 def table2_leg(iters=5):
-    """Forward-only timings at the shape of the pages' kernel table (B=1, d=64, G=8, Hq=64,
-    Hk=8, L=64, causal; T from 4096 to 65536), each against an L=0 forward on the same
-    sequence inputs.  The pages time forward + backward of Triton kernels on another GPU,
-    so only the trend of the extra time with T is comparable; both conventions are given:
-    (t - t0) / t as in the pages' table and (t - t0) / t0."""
+    """Timings at the shape of the pages' kernel table (B=1, d=64, G=8, Hq=64, Hk=8, L=64,
+    causal; T from 4096 to 65536), each against L=0 on the same sequence inputs: the
+    forward alone, and forward + backward as the pages time it (their figures are Triton
+    kernels on another GPU, so only the trend of the extra time with T is comparable).
+    Both conventions are given: (t - t0) / t as in the pages' table and (t - t0) / t0."""
     stream = torch.cuda.current_stream()
 
     def timed(fn):
@@ -581,20 +581,40 @@ def table2_leg(iters=5):
         def run0():
             api.moda_attn_fwd(dev["q"], dev["k_seq"], dev["v_seq"], None, None, causal=True, out=out, lse=lse)
 
-        run(), run0()
-        t, t0 = [], []
+        dout = I.random_dout(shape, 8100, device="cuda")
+        grads = (torch.empty_like(dev["q"]), torch.empty_like(dev["k_seq"]), torch.empty_like(dev["v_seq"]),
+                 torch.empty_like(kd), torch.empty_like(vd))
+        ws = torch.empty(api.moda_attn_bwd_workspace(1, T, 64, 8, 64, 64), dtype=torch.uint8, device="cuda")
+
+        def run_fb():
+            run()
+            api.moda_attn_bwd(dev["q"], dev["k_seq"], dev["v_seq"], kd, vd, out, lse, dout, causal=True,
+                              grads=grads, workspace=ws)
+
+        def run0_fb():
+            run0()
+            api.moda_attn_bwd(dev["q"], dev["k_seq"], dev["v_seq"], None, None, out, lse, dout, causal=True,
+                              grads=grads[:3] + (None, None), workspace=ws)
+
+        run(), run0(), run_fb(), run0_fb()
+        t, t0, tb, tb0 = [], [], [], []
         for _ in range(iters):
             t.append(timed(run))
             t0.append(timed(run0))
+            tb.append(timed(run_fb))
+            tb0.append(timed(run0_fb))
         ms, ms0 = float(np.median(t)), float(np.median(t0))
+        fb, fb0 = float(np.median(tb)), float(np.median(tb0))
         rows.append({"T": T, "ms": round(ms, 4), "l0_ms": round(ms0, 4),
                      "extra_over_t": round((ms - ms0) / ms, 4), "extra_over_t0": round((ms - ms0) / ms0, 4),
                      "time_ratio_l0_over_moda": round(ms0 / ms, 4),
-                     "tflops": round(acc.flops(shape) / (ms * 1e-3) / 1e12, 1)})
-        del dev, kd, vd, out, lse
+                     "tflops": round(acc.flops(shape) / (ms * 1e-3) / 1e12, 1),
+                     "fwd_bwd_ms": round(fb, 4), "fwd_bwd_l0_ms": round(fb0, 4),
+                     "fwd_bwd_extra_over_t": round((fb - fb0) / fb, 4)})
+        del dev, kd, vd, out, lse, dout, grads, ws
         torch.cuda.empty_cache()
-    return {"workload": "forward at the pages' kernel-table shape B=1 d=64 G=8 Hq=64 Hk=8 L=64 causal, "
-                        "T=4096..65536, each against L=0 on the same inputs", "rows": rows}
+    return {"workload": "forward, and forward + backward, at the pages' kernel-table shape B=1 d=64 G=8 Hq=64 "
+                        "Hk=8 L=64 causal, T=4096..65536, each against L=0 on the same inputs", "rows": rows}
 
 
 def main():

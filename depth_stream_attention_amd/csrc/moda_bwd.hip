@@ -447,8 +447,13 @@ __device__ __forceinline__ void dq_tile(f32x16 (&dqa)[D / 32], const bf16x8 (&qf
   }
 }
 
+// Waves per SIMD the dq kernel is compiled for: at d = 64 it fits three
+// (at most 168 VGPRs, 32 KiB of LDS per workgroup).
+template <int D>
+constexpr int kDqWavesPerEU = D == 64 ? 3 : 2;
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void moda_bwd_dq_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDqWavesPerEU<D>, kDqWavesPerEU<D>))) void moda_bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ ws_l2, const float* __restrict__ ws_dd,
     const float* __restrict__ dq_depth, int B, int T, int Hq, int Hk, int lgG, int nrb, float scale,
