@@ -891,31 +891,35 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
   // No row of tile it sees the pair's keys.
   auto skip = [&](int it) __attribute__((always_inline)) { return CAUSAL && ((it * kBN + kBN - 1) >> lgG) < kw0; };
 
-  // Step u (u = 0 .. nt - i0) publishes tile i0 + u, starts loading the next
-  // one, lets the P waves work on tile i0 + u and the dS waves on tile
-  // i0 + u - 1.  Tile i0 + u lives in stage and slot u % 3; the steps are
+  // Row tiles are taken last to first, so every workgroup starts at the same
+  // tile and the workgroups that run side by side on one XCD (the same
+  // (b, hk)) read the same Q/dO rows at about the same time.  Step u
+  // (u = 0 .. nt - i0) publishes tile nt - 1 - u, starts loading the next
+  // one, lets the P waves work on tile nt - 1 - u and the dS waves on tile
+  // nt - u.  The tile of step u lives in stage and slot u % 3; the steps are
   // unrolled by three so that the residue, and with it every LDS offset, is a
-  // constant.  The masked steps are rounded up to a multiple of three (the
-  // mask is exact on any tile, so the extra steps only cost a select).
+  // constant.  The unmasked steps are rounded down to a multiple of three and
+  // the rest run masked (the mask is exact on any tile, so the extra masked
+  // steps only cost a select).
   using IC0 = std::integral_constant<int, 0>;
   using IC1 = std::integral_constant<int, 1>;
   using IC2 = std::integral_constant<int, 2>;
   const int n_it = nt - i0 + 1;
-  const int n_mask = min(n_it, (i_m - i0 + 2) / 3 * 3);
+  const int n_unm = CAUSAL ? (nt - i_m) / 3 * 3 : n_it;
   auto p_step = [&](auto res, auto maskc, int u) __attribute__((always_inline)) {
     constexpr int R = decltype(res)::value;
     constexpr bool MASK = decltype(maskc)::value != 0;
-    const int it = i0 + u;
+    const int it = nt - 1 - u;
     publish_tile();
-    if (it + 1 < nt) dma_rows<D>(qb, ob, l2b, ddb, T, Hq, lgG, TG, it + 1, smem, (R + 1) % 3, pair, lane, dm);
-    if (it >= nt || skip(it)) return;
+    if (it - 1 >= i0) dma_rows<D>(qb, ob, l2b, ddb, T, Hq, lgG, TG, it - 1, smem, (R + 1) % 3, pair, lane, dm);
+    if (it < i0 || skip(it)) return;
     p_tile<D, MASK, R * LY::TB, R * LY::SB, R * XS::BYTES>(acc, frag, ra, stat0, xfer0, it * kBN, lgG, my_key, half,
                                                            scale_log2);
   };
   auto ds_step = [&](auto res, auto maskc, int u) __attribute__((always_inline)) {
     constexpr int R = (decltype(res)::value + 2) % 3;  // the previous tile's stage and slot
     publish_tile();
-    const int jt = i0 + u - 1;
+    const int jt = nt - u;
     if (u == 0 || skip(jt)) return;
     ds_tile<D, R * LY::TB, R * LY::SB, R * XS::BYTES>(acc, frag, ra, stat0, xfer0, half);
   };
@@ -930,14 +934,14 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     if (u < end) step(IC1(), maskc, u++);
   };
 
-  if (p_role && i0 < nt) dma_rows<D>(qb, ob, l2b, ddb, T, Hq, lgG, TG, i0, smem, 0, pair, lane, dm);
+  if (p_role && i0 < nt) dma_rows<D>(qb, ob, l2b, ddb, T, Hq, lgG, TG, nt - 1, smem, 0, pair, lane, dm);
   int u = 0;
   if (p_role) {
-    run(p_step, IC1(), u, n_mask);
-    run(p_step, IC0(), u, n_it);
+    run(p_step, IC0(), u, n_unm);
+    run(p_step, IC1(), u, n_it);
   } else {
-    run(ds_step, IC1(), u, n_mask);
-    run(ds_step, IC0(), u, n_it);
+    run(ds_step, IC0(), u, n_unm);
+    run(ds_step, IC1(), u, n_it);
   }
 
   if (my_key < T) {
