@@ -26,7 +26,10 @@
 //         wave's own tokens, read from the packed [B][T][Hk][L][d] stream (each
 //         (token, KV head) slab is one contiguous run, each depth element is
 //         read from HBM exactly once and used by the G rows of its token
-//         only), spread evenly among the sequence tiles.
+//         only), spread evenly among the sequence tiles.  With d = 128 and
+//         G <= 16 a depth tile's scores are one 16x16x32 block per wave (the
+//         16 slots against the 16-row half of the wave that holds the token),
+//         permuted into the 32x32 layout of the sequence scores.
 //     Both kinds fold into the same running (max, sum, output) state of each
 //     row, so the softmax is one joint softmax over both candidate sets.
 //   * Scores are computed transposed, S^T = K * Q^T, on 32x32x16 bf16 MFMA with
@@ -307,6 +310,32 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(kWavesPe
   // wave/2, score registers [8*(wave%2), 8*(wave%2) + 8).
   const int dj = wave >> 1, dh = wave & 1;
 
+  // With d = 128 and G <= 16 a depth tile's scores are one 16x16 block per
+  // wave (v_mfma_f32_16x16x32_bf16): the wave's 16 slots against the 16-row
+  // half of its rows that holds the token (G <= 16 rows, a power of two, so
+  // they never straddle the halves).  The B operand is Q^T of that half in
+  // the 16x16 layout -- lane l: row 16*qh + l%16, d = 32c + 8*(l/16) + [0, 8)
+  // -- read from global memory (the rows are L2-resident since the prologue)
+  // whenever the half changes, one depth tile ahead.  The 32x32 block of the
+  // sequence path would spend 32 keys x 32 rows on the same 16 slots x G rows.
+  constexpr bool kDepth16 = DEPTH && D == 128;
+  const bool depth16 = kDepth16 && lgG <= 4;
+  bf16x8 q16[D / 32];
+  auto half_of = [&](int d) { return ((d / nchunk) << lgG) >> 4; };
+  auto load_q16 = [&](int qh) __attribute__((always_inline)) {
+    const int row = wrow0 + 16 * qh + (lane & 15);
+    const bool ok = row < TG;
+    const uint16_t* qr = q + ((static_cast<int64_t>(b) * T + (row >> lgG)) * Hq + hk * G + (row & (G - 1))) * D +
+                         8 * (lane >> 4);
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      u32x4 val = {0u, 0u, 0u, 0u};
+      if (ok) val = *reinterpret_cast<const u32x4*>(qr + 32 * c);
+      q16[c] = __builtin_bit_cast(bf16x8, val);
+    }
+  };
+  if (depth16 && nd > 0) load_q16(0);
+
   // The LDS buffer of pipeline position pos is smem + (pos & 1) * 2 * BYTES.
   // Sequence tiles run in pairs with a constant buffer each (seq_run); the
   // depth tiles, one per run, take the buffer at run time, with its base
@@ -390,16 +419,53 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(kWavesPe
       }
       ++pos;
       const TileAddr<D> ta = tile_addr<D, W>(cur, lo);
-      const f32x16 sacc = qk_block<D>(qf, ta.k, 32 * dj * TL::ROW_BYTES);
       const int dtok = d / nchunk;
       const int slot0 = (d - dtok * nchunk) * kDepthRowsPerWave;
       const bool mine = my_t == wt0 + dtok;
       const int hf = opaque(half);
+      // s[i]: slot slot0 + 8*(i/4) + 4*hf + i%4 of this lane's row (the
+      // weights' order in the PV operand).
       float s[8];
+      if (kDepth16 && depth16) {
+        // S^T (16 slots x 16 rows): A = the wave's 16 depth rows, row l%16,
+        // logical chunk 4c + l/16; lane l gets slots 4*(l/16) + [0, 4) of row
+        // 16*qh + l%16.
+        const int kr = 16 * wave + (lane & 15);
+        const uint32_t kbase = lds_addr(cur) + kr * TL::ROW_BYTES;
+        f32x4 s4 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) {
+          const bf16x8 a = *lds_at<lds_bf16x8_t>(kbase + (((4 * c + (lane >> 4)) ^ TL::swz_k(kr)) * 16));
+          s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, q16[c], s4, 0, 0, 0);
+        }
+        if (d + 1 < nd && half_of(d + 1) != half_of(d)) load_q16(half_of(d + 1));
+        // To the 32x32 layout: lane L (row L%32, hf = L/32) needs slots 4hf + [0, 4)
+        // and 8 + 4hf + [0, 4) of its row, held by lanes 16hf + L%16 and
+        // 32 + 16hf + L%16.  Swapping 16-lane rows (odd of the first operand with
+        // even of the second), then 32-lane halves, leaves exactly those in the
+        // two operands (rows of the other half are masked below).
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // (Elements go through scalars: __builtin_bit_cast of a vector
+          // element reads element 0.)
+          const float si = s4[i];
+          const uint32_t x = __builtin_bit_cast(uint32_t, si);
+          const auto r16 = __builtin_amdgcn_permlane16_swap(x, static_cast<uint32_t>(opaque(static_cast<int>(x))),
+                                                            false, false);
+          const auto r32 = __builtin_amdgcn_permlane32_swap(r16[0], r16[1], false, false);
+          const uint32_t lo = r32[0], hi = r32[1];
+          s[i] = __builtin_bit_cast(float, lo);
+          s[4 + i] = __builtin_bit_cast(float, hi);
+        }
+      } else {
+        const f32x16 sacc = qk_block<D>(qf, ta.k, 32 * dj * TL::ROW_BYTES);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s[i] = sacc[8 * dh + i];
+      }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int slot = slot0 + 8 * (i >> 2) + 4 * hf + (i & 3);
-        s[i] = (mine && slot < L) ? sacc[8 * dh + i] : -INFINITY;
+        s[i] = (mine && slot < L) ? s[i] : -INFINITY;
       }
       bf16x8 pb[1];
       online_update<D, 8>(st, s, pb, scale_log2);
