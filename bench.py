@@ -446,6 +446,44 @@ def backward_leg(shape, dev, kd, vd, out, lse, out0, lse0, iters=4):
                          "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
 
 
+def comparator_leg(dev, out0, iters=5):
+    """Context only: PyTorch's own flash-attention SDPA backend (restricted to that backend, so
+    it raises rather than fall back to another path) on the L=0 shape of the long-context
+    layer, with the same q / k_seq / v_seq, against this library's L=0 forward."""
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    shape0 = I.workload(5, 1)
+    q = dev["q"].transpose(1, 2).contiguous()  # [B,Hq,T,d]
+    k = dev["k_seq"].transpose(1, 2).contiguous()
+    v = dev["v_seq"].transpose(1, 2).contiguous()
+    stream = torch.cuda.current_stream()
+    res = {"workload": "causal GQA attention B=1 T=65536 Hq=16 Hk=4 d=128 (the L=0 shape)",
+           "impl": "torch.nn.functional.scaled_dot_product_attention, FLASH_ATTENTION backend, enable_gqa"}
+    try:
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            def run():
+                return torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True, enable_gqa=True)
+            o = run()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(iters):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                run()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+    except RuntimeError as ex:  # the backend does not take this shape on this build
+        res["error"] = str(ex).splitlines()[0][:200]
+        return res
+    ms = float(np.median(ts))
+    res.update({"ms": round(ms, 3), "tflops": round(acc.flops(shape0) / (ms * 1e-3) / 1e12, 1),
+                "max_abs_diff_vs_moda_l0_out": float((o.transpose(1, 2).float() - out0.float()).abs().max()),
+                "note": "median of %d HIP-event-timed calls; context, not a target" % iters})
+    del q, k, v, o
+    torch.cuda.empty_cache()
+    return res
+
+
 KVPROJ_SHAPE = dict(B=1, T=65536, Dm=2048, Hk=4, d=128)
 
 
@@ -628,6 +666,8 @@ def main():
     ap.add_argument("--no-peaks", action="store_true", help="skip the attainable-peak measurement kernels")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
     ap.add_argument("--no-depth-write", action="store_true", help="skip the depth-write (KV projection) measurement")
+    ap.add_argument("--no-comparator", action="store_true",
+                    help="skip the context timing of PyTorch's flash-attention SDPA at the L=0 shape")
     ap.add_argument("--table2", action="store_true",
                     help="only time the forward at the pages' kernel-table shape over T and print that JSON line")
     ap.add_argument("--no-workloads", action="store_true",
@@ -741,6 +781,8 @@ def main():
         rec["roofline"]["frac_of_measured_peak"] = round(tflops / rec["measured_peaks"]["mfma_bf16_tflops"], 4)
     if not args.no_backward:
         rec["backward"] = backward_leg(shape, dev, kd, vd, out, lse, out0, lse0)
+    if not args.no_comparator:
+        rec["comparator"] = comparator_leg(dev, out0)
     if not args.no_decode:
         rec["decode"] = decode_leg()
     if not args.no_depth_write:  # last: it overwrites the final depth slot of the step's buffers
