@@ -58,10 +58,12 @@ def test_keys_scaled_by_half():
     full_parity(S(1, 300, 8, 4, 128, 32, key_scale=0.5), 60)
 
 
-@pytest.mark.parametrize("G", [1, 4])
-def test_depth_aligned_stress(G):
-    # head hk*G's depth keys track its query, so depth carries most of its mass at every t
-    full_parity(S(1, 700, 4 * G, 4, 128, 12), 70 + G, depth_aligned=True)
+@pytest.mark.parametrize("G,L", [(1, 12), (4, 12), (1, 40), (2, 40), (8, 40), (16, 40)])
+def test_depth_aligned_stress(G, L):
+    # head hk*G's depth keys track its query, so depth carries most of its mass at every t;
+    # L = 40 gives each token three 16-slot depth tiles (the last one partial), and with
+    # G <= 16 a wave's tokens fill both 16-row halves of its rows
+    full_parity(S(1, 700, 4 * G, 4, 128, L), 70 + G + L, depth_aligned=True)
 
 
 def test_several_tiles_multi_batch():
