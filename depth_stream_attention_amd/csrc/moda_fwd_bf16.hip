@@ -453,9 +453,9 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(kWavesPe
           const auto r16 = __builtin_amdgcn_permlane16_swap(x, static_cast<uint32_t>(opaque(static_cast<int>(x))),
                                                             false, false);
           const auto r32 = __builtin_amdgcn_permlane32_swap(r16[0], r16[1], false, false);
-          const uint32_t lo = r32[0], hi = r32[1];
-          s[i] = __builtin_bit_cast(float, lo);
-          s[4 + i] = __builtin_bit_cast(float, hi);
+          const uint32_t lo32 = r32[0], hi32 = r32[1];
+          s[i] = __builtin_bit_cast(float, lo32);
+          s[4 + i] = __builtin_bit_cast(float, hi32);
         }
       } else {
         const f32x16 sacc = qk_block<D>(qf, ta.k, 32 * dj * TL::ROW_BYTES);
